@@ -1,0 +1,100 @@
+"""Expert SwiGLU FFN on FP8 inputs and the DeepSeekMoE layer forward.
+
+Sources:
+* V3 notes §2: the MoE layer has one shared expert that every token passes
+  through plus 256 routed experts of intermediate size 2048, 8 chosen per
+  token; the layer output sums the shared expert's output and the routed
+  experts' outputs weighted by their gates (the equation itself was lost from
+  the page; only "just the 8 top-K gates are non-zero" survives).
+* V3 notes §6: the Linear GEMMs run with FP8 inputs and produce BF16/FP32
+  outputs; the activation between the two projections is quantised again as
+  the down-projection's FP8 input, per 1x128 tile (§6.1).
+* infra answer (memory paragraph): SwiGLU is the expert activation (named as
+  a recomputation target).
+
+Readings taken where the pages are silent:
+* W13 of an expert is [2I][H]: rows 0..I-1 are the gate projection, rows
+  I..2I-1 the up projection; a = silu(gate) * up with silu(v) = v/(1+e^-v);
+* a is evaluated in float64, rounded once to float32, then 1x128-quantised;
+* the shared expert has the same intermediate size I and gate 1;
+* the router is not quantised: logits are bf16 x times bf16 router weights,
+  evaluated here in float64 (the GPU accumulates in FP32);
+* no residual add: the layer returns the FFN output only;
+* every (token, expert) pair is computed (no capacity limit, no dropping).
+"""
+
+import numpy as np
+
+from .gemm import block_scaled_gemm, gemm_normaliser
+from .quant import quant_act_1x128
+from .route import permute, route
+
+
+def expert_ffn(qx, sx, q13, s13, q2, s2):
+    """One expert on quantised input rows.
+
+    qx uint8 [n][H], sx f32 [n][H/128]; q13 uint8 [2I][H], s13 f32
+    [2I/128][H/128]; q2 uint8 [H][I], s2 f32 [H/128][I/128].
+    Returns (o float64 [n][H], d float64 [n][H]) where d is the down
+    projection's |a_hat| x |w2_hat| normaliser.
+    """
+    inter = q13.shape[0] // 2
+    h = block_scaled_gemm(qx, sx, q13, s13)                  # [n][2I]
+    gate, up = h[:, :inter], h[:, inter:]
+    with np.errstate(over="ignore"):
+        a = gate / (1.0 + np.exp(-gate)) * up
+    a32 = a.astype(np.float32)
+    qa, sa = quant_act_1x128(a32)
+    o = block_scaled_gemm(qa, sa, q2, s2)
+    d = gemm_normaliser(qa, sa, q2, s2)
+    return o, d
+
+
+def router_logits(x, router_w):
+    """z = x . Wr^T in float64, with its normaliser |x| . |Wr|^T."""
+    x64 = np.asarray(x, np.float64)
+    w64 = np.asarray(router_w, np.float64)
+    return x64 @ w64.T, np.abs(x64) @ np.abs(w64).T
+
+
+def moe_layer(x, router_w, bias, get_expert, shared, n_groups, groups_kept, top_k,
+              logits=None):
+    """DeepSeekMoE layer forward for the rows of x.
+
+    x           float32 [T][H] holding bf16 values
+    router_w    float32 [E][H] holding bf16 values
+    bias        float32 [E]
+    get_expert  callable e -> (q13, s13, q2, s2) for routed expert e
+    shared      (q13, s13, q2, s2) of the shared expert
+    logits      optional float32 [T][E]; when given, routing uses them instead
+                of the oracle's own float64 logits rounded to float32
+
+    Returns a dict: qx, sx, logits64, logits_d, topk_idx, gates, counts,
+    offsets, perm, inv, y (float64 [T][H]) and y_d (its normaliser).
+    """
+    x = np.asarray(x, np.float32)
+    t, h = x.shape
+    n_experts = np.asarray(router_w).shape[0]
+    qx, sx = quant_act_1x128(x)
+    z64, zd = router_logits(x, router_w)
+    z32 = z64.astype(np.float32) if logits is None else np.asarray(logits, np.float32)
+    r = route(z32, bias, n_groups, groups_kept, top_k)
+    counts, offsets, perm, inv = permute(r["topk_idx"], n_experts)
+
+    y, y_d = expert_ffn(qx, sx, *shared)                       # shared expert, gate 1
+    for e in range(n_experts):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        if rows.size == 0:
+            continue
+        o, d = expert_ffn(qx[rows], sx[rows], *get_expert(e))
+        kpos = np.argmax(r["topk_idx"][rows] == e, axis=1)
+        g = r["gates"][rows, kpos][:, None]
+        y[rows] += g * o
+        y_d[rows] += g * d
+
+    return {
+        "qx": qx, "sx": sx, "logits64": z64, "logits_d": zd,
+        "topk_idx": r["topk_idx"], "gates": r["gates"],
+        "counts": counts, "offsets": offsets, "perm": perm, "inv": inv,
+        "y": y, "y_d": y_d,
+    }
