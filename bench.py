@@ -1,0 +1,240 @@
+"""Benchmark of the DeepSeekMoE FP8 layer forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload v3_prefill]
+
+A step is one pass of the whole hot path over one batch: dsmoe_moe_forward
+(1x128 quantisation of x, router logits, group-limited top-8 routing,
+permute, gate/up FP8 GEMM with SwiGLU and requantisation, routed and shared
+down FP8 GEMMs, combine) followed by dsmoe_update_bias.  Weights are
+quantised once before timing (dsmoe_quant_w_128x128 over every expert; its
+time is reported separately as quant_w_ms).  Inputs are seeded synthetic
+tensors already resident in HBM.  Prints one JSON line on stdout; progress
+goes to stderr.
+"""
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + grouped-GEMM FP8 TFLOP/s (% MFMA peak / % HBM BW) @1 GPU"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+RIDGE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="v3_prefill",
+                    choices=["v3_prefill", "v3_decode", "v3_skew", "tiny"])
+    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2)
+    return ap.parse_args()
+
+
+def build_layer(cfg, d, torch, dsi):
+    """Device inputs and FP8 weights; returns (x, bias, weights, quant_w_ms)."""
+    E, H, I = cfg.E, cfg.H, cfg.I
+    x, wr, bias = dsi.layer_activations_device(cfg, "cuda")
+    if cfg.name == "tiny":
+        inp = dsi.layer_inputs_host(cfg, 0)
+        w13_all = torch.from_numpy(inp["w13"]).to(torch.bfloat16).cuda()
+        w2_all = torch.from_numpy(inp["w2"]).to(torch.bfloat16).cuda()
+    else:
+        w13_all = torch.empty((E + 1, 2 * I, H), dtype=torch.bfloat16, device="cuda")
+        w2_all = torch.empty((E + 1, H, I), dtype=torch.bfloat16, device="cuda")
+        for e in range(E + 1):
+            a, b = dsi.expert_weights_device(cfg, e, "cuda")
+            w13_all[e].copy_(a)
+            w2_all[e].copy_(b)
+            del a, b
+    q13 = torch.empty((E + 1, 2 * I, H), dtype=torch.uint8, device="cuda")
+    s13 = torch.empty((E + 1, 2 * I // 128, H // 128), dtype=torch.float32, device="cuda")
+    q2 = torch.empty((E + 1, H, I), dtype=torch.uint8, device="cuda")
+    s2 = torch.empty((E + 1, H // 128, I // 128), dtype=torch.float32, device="cuda")
+    times = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        d.quant_w_128x128(w13_all, q13, s13)
+        d.quant_w_128x128(w2_all, q2, s2)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del w13_all, w2_all
+    torch.cuda.empty_cache()
+    weights = d.MoEWeights(q13[:E], s13[:E], q2[:E], s2[:E], q13[E], s13[E], q2[E], s2[E], wr)
+    return x, bias, weights, statistics.median(times)
+
+
+def cpu_baseline(cfg, n_tokens, torch, dsi):
+    """The oracle, as it stands, on a bounded sample: n_tokens tokens of the
+    same batch through the whole layer (weight quantisation excluded, as on
+    the GPU side)."""
+    import numpy as np
+    from oracle import layer as ol
+    from oracle import quant as oq
+    from oracle import route as orr
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    inp = dsi.layer_inputs_host(cfg, 0, with_weights=False)
+    xs = inp["x"][:n_tokens]
+    z, _ = ol.router_logits(xs, inp["router_w"])
+    r = orr.route(z.astype(np.float32), inp["bias"], cfg.G, cfg.Mg, cfg.K)
+    needed = sorted(set(r["topk_idx"].reshape(-1).tolist()) | {cfg.E})
+    cache = {}
+    for e in needed:
+        if cfg.name == "tiny":
+            full = dsi.layer_inputs_host(cfg, 0)
+            a, b = full["w13"][e], full["w2"][e]
+        else:
+            at, bt = dsi.expert_weights_device(cfg, e, "cuda")
+            a, b = at.float().cpu().numpy(), bt.float().cpu().numpy()
+        q13, s13 = oq.quant_w_128x128(a)
+        q2, s2 = oq.quant_w_128x128(b)
+        cache[e] = (q13, s13, q2, s2)
+    log(f"cpu baseline: oracle on {n_tokens} tokens, {len(needed)} experts")
+    t0 = time.perf_counter()
+    ol.moe_layer(xs, inp["router_w"], inp["bias"], lambda e: cache[e], cache[cfg.E], cfg.G, cfg.Mg, cfg.K)
+    dt = time.perf_counter() - t0
+    return {
+        "value": n_tokens / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+        "sample": f"{n_tokens} tokens of the {cfg.name} batch through the whole layer "
+                  f"({len(needed)} experts incl. shared; float64 NumPy; weight quantisation excluded), "
+                  f"{dt:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fp8_block_scaled_dsmoe_amd as d
+    import dsmoe_inputs as dsi
+
+    cfg = dsi.LAYER_CONFIGS[args.workload]
+    out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+    T, H, I, E, K = cfg.T, cfg.H, cfg.I, cfg.E, cfg.K
+    log(f"workload {cfg.name}: T={T} H={H} E={E} G={cfg.G} Mg={cfg.Mg} K={K} I={I}")
+    x, bias, weights, quant_w_ms = build_layer(cfg, d, torch, dsi)
+    log(f"weights quantised: {quant_w_ms:.2f} ms for {E + 1} experts")
+    desc = d.MoEDesc(H, I, E, cfg.G, cfg.Mg, K, 1)
+    ws = torch.empty((d.moe_workspace_bytes(desc, T),), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, H), dtype=out_dtype, device="cuda")
+    counts = torch.empty((E,), dtype=torch.int32, device="cuda")
+
+    def step(ev=None):
+        d.moe_forward(desc, weights, bias, x, y=y, counts=counts, workspace=ws,
+                      stage_events=None if ev is None else [e.cuda_event for e in ev])
+        d.update_bias(bias, counts, T, K, 0.001)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    counts_first = counts.cpu().numpy()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(d.STAGE_EVENTS)] for _ in range(args.steps)]
+    for row in ev:
+        for e in row:
+            e.record()          # creates the underlying event
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(ev[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    stage_ms = {}
+    for s_i, name in enumerate(d.STAGES):
+        stage_ms[name] = statistics.mean(r[s_i].elapsed_time(r[s_i + 1]) for r in ev)
+    log(f"{args.steps} steps: {ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}); stages " +
+        ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
+
+    import numpy as np
+    counts_last = counts.cpu().numpy()
+    touched = int(np.count_nonzero(counts_last))
+    rows1 = T * K + T
+    # algorithmic work
+    gemm_flops = 6.0 * rows1 * H * I                      # gate/up + down, routed + shared
+    w_bytes = (touched + 1) * 3 * H * I                   # FP8 weights of the experts touched
+    s_bytes = (touched + 1) * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128)) * 4
+    io_bytes = T * H * 2 + T * H * (2 if out_dtype == torch.bfloat16 else 4) + E * H * 2
+    layer_bytes = w_bytes + s_bytes + io_bytes
+    tok_s = T / (ms_step * 1e-3)
+    # dominant kernel: gate/up GEMM + SwiGLU + requant
+    g1_flops = 2.0 * rows1 * H * 2 * I
+    g1_bytes = ((touched + 1) * 2 * I * H + (touched + 1) * (2 * I // 128) * (H // 128) * 4 +
+                T * H + T * (H // 128) * 4 + rows1 * I + rows1 * (I // 128) * 4)
+    g1_ms = stage_ms["gemm1_swiglu_requant"]
+    g1_bound = "hbm" if g1_flops / g1_bytes < RIDGE else "mfma"
+    if g1_bound == "hbm":
+        achieved, peak, unit = g1_bytes / (g1_ms * 1e-3) / 1e9, PEAK_HBM_GBPS, "GB/s"
+    else:
+        achieved, peak, unit = g1_flops / (g1_ms * 1e-3) / 1e12, PEAK_FP8_TFLOPS, "TFLOP/s"
+    gemm_ms = g1_ms + stage_ms["gemm2_routed"] + stage_ms["gemm2_shared_combine"]
+
+    result = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: DeepSeekMoE layer forward + bias update, T={T}, H={H}, "
+                               f"E={E} in G={cfg.G} groups, top-{K} within {cfg.Mg} groups, "
+                               f"1 shared expert, I={I}, y {args.out_dtype}",
+                   "T": T, "H": H, "E": E, "G": cfg.G, "Mg": cfg.Mg, "K": K, "I": I},
+        "roofline": {"bound": g1_bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "gemm_kernel<256, SwiGLU-requant> (gate/up GEMM)",
+                     "algorithmic_bytes": int(g1_bytes), "algorithmic_flops": g1_flops,
+                     "avg_ms": round(g1_ms, 4)},
+        "grouped_gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2),
+        "grouped_gemm_frac_mfma_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+        "layer_tflops": round(gemm_flops / (ms_step * 1e-3) / 1e12, 2),
+        "layer_frac_mfma_peak": round(gemm_flops / (ms_step * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+        "layer_hbm_gbps": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "layer_frac_hbm_peak": round(layer_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "layer_algorithmic_bytes": int(layer_bytes),
+        "experts_touched": touched,
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "quant_w_ms": round(quant_w_ms, 3),
+        "load_imbalance": {"max_over_mean_first": round(float(counts_first.max() / counts_first.mean()), 3),
+                           "max_over_mean_last": round(float(counts_last.max() / counts_last.mean()), 3),
+                           "zero_load_experts_last": int((counts_last == 0).sum())},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens, torch, dsi)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

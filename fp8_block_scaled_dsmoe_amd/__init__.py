@@ -1,0 +1,330 @@
+"""Python binding of libdsmoe.so: the DeepSeekMoE FFN layer forward on the
+fine-grained FP8 recipe, as hand-written HIP kernels for MI355X (gfx950).
+
+Argument marshalling only.  Every step runs inside the HIP library; PyTorch is
+used for device memory and the current stream.  Each wrapper checks dtypes,
+devices, contiguity and shapes, allocates outputs that were not passed in,
+and calls the C function of the same name (include/dsmoe.h).  A non-zero
+status raises DsmoeError.  There is no fallback: if the library is missing,
+importing this package fails.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "DsmoeError", "MoEDesc", "MoEWeights", "LIB_PATH", "lib",
+    "quant_act_1x128", "quant_w_128x128", "route", "fp8_grouped_gemm",
+    "moe_workspace_bytes", "moe_forward", "update_bias", "quantize_layer_weights",
+    "BF16", "F32",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsmoe.so")
+BF16, F32 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m fp8_block_scaled_dsmoe_amd.build` "
+        "(hipcc, gfx950). There is no non-HIP fallback.")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _i32, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_size_t
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("H", _i64), ("I", _i64), ("E", _i32), ("G", _i32), ("Mg", _i32), ("K", _i32),
+                ("n_shared", _i32)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("w13", "s13", "w2", "s2", "w13_sh", "s13_sh", "w2_sh", "s2_sh",
+                                   "router_w")]
+
+
+class _Debug(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("qx", "sx", "logits", "topk_idx", "gates", "offsets", "perm", "inv")] + \
+               [("stage_events", ctypes.POINTER(_vp))]
+
+
+STAGE_EVENTS = 8
+STAGES = ("quant_x", "router_logits", "route_select", "permute", "gemm1_swiglu_requant",
+          "gemm2_routed", "gemm2_shared_combine")
+
+
+lib.dsmoe_status_str.restype = ctypes.c_char_p
+lib.dsmoe_status_str.argtypes = [_int]
+lib.dsmoe_abi_version.restype = _int
+lib.dsmoe_abi_version.argtypes = []
+lib.dsmoe_quant_act_1x128.restype = _int
+lib.dsmoe_quant_act_1x128.argtypes = [_vp, _int, _i64, _i64, _vp, _vp, _vp]
+lib.dsmoe_quant_w_128x128.restype = _int
+lib.dsmoe_quant_w_128x128.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp]
+lib.dsmoe_route.restype = _int
+lib.dsmoe_route.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+lib.dsmoe_fp8_grouped_gemm.restype = _int
+lib.dsmoe_fp8_grouped_gemm.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64, _vp, _int, _vp]
+lib.dsmoe_moe_workspace_bytes.restype = _sz
+lib.dsmoe_moe_workspace_bytes.argtypes = [ctypes.POINTER(_Desc), _i64]
+lib.dsmoe_moe_forward.restype = _int
+lib.dsmoe_moe_forward.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Weights), _vp, _vp, _i64, _vp,
+                                  _int, _vp, _vp, _sz, ctypes.POINTER(_Debug), _vp]
+lib.dsmoe_update_bias.restype = _int
+lib.dsmoe_update_bias.argtypes = [_vp, _vp, _i32, _i64, _i32, ctypes.c_float, _vp]
+
+EXPORTED = ("dsmoe_status_str", "dsmoe_abi_version", "dsmoe_quant_act_1x128", "dsmoe_quant_w_128x128",
+            "dsmoe_route", "dsmoe_fp8_grouped_gemm", "dsmoe_moe_workspace_bytes", "dsmoe_moe_forward",
+            "dsmoe_update_bias")
+
+
+class DsmoeError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {lib.dsmoe_status_str(status).decode()} ({status})")
+
+
+def _check(status: int, call: str):
+    if status != 0:
+        raise DsmoeError(status, call)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _dtype_code(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return BF16
+    if dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def _out_dtype(code: int):
+    return torch.float32 if code == F32 else torch.bfloat16
+
+
+# ---------------------------------------------------------------------------
+
+def quant_act_1x128(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+                    scale: Optional[torch.Tensor] = None):
+    """x [rows][cols] bf16/f32 -> (q uint8 [rows][cols], scale f32 [rows][cols/128])."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    _dev(x, x.dtype, "x")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
+    scale = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device) if scale is None else scale
+    _dev(q, torch.uint8, "q")
+    _dev(scale, torch.float32, "scale")
+    _check(lib.dsmoe_quant_act_1x128(_p(x), _dtype_code(x.dtype), rows, cols, _p(q), _p(scale), _stream()),
+           "dsmoe_quant_act_1x128")
+    return q, scale
+
+
+def quant_w_128x128(w: torch.Tensor, q: Optional[torch.Tensor] = None,
+                    scale: Optional[torch.Tensor] = None):
+    """w [n_mats][N][K] (or [N][K]) -> (q uint8 same shape, scale f32 [n_mats][N/128][K/128])."""
+    squeeze = w.dim() == 2
+    w3 = w.unsqueeze(0) if squeeze else w
+    if w3.dim() != 3:
+        raise ValueError("w must be 2-D or 3-D")
+    _dev(w3, w.dtype, "w")
+    nm, n, k = w3.shape
+    q = torch.empty(w3.shape, dtype=torch.uint8, device=w.device) if q is None else q.view(nm, n, k)
+    scale = (torch.empty((nm, n // 128, k // 128), dtype=torch.float32, device=w.device)
+             if scale is None else scale.view(nm, n // 128, k // 128))
+    _dev(q, torch.uint8, "q")
+    _dev(scale, torch.float32, "scale")
+    _check(lib.dsmoe_quant_w_128x128(_p(w3), _dtype_code(w.dtype), nm, n, k, _p(q), _p(scale), _stream()),
+           "dsmoe_quant_w_128x128")
+    if squeeze:
+        return q[0], scale[0]
+    return q, scale
+
+
+def route(logits: torch.Tensor, bias: torch.Tensor, n_groups: int, groups_kept: int, top_k: int):
+    """logits f32 [T][E], bias f32 [E] -> dict of topk_idx, gates, counts, offsets, perm, inv."""
+    _dev(logits, torch.float32, "logits")
+    _dev(bias, torch.float32, "bias")
+    t, e = logits.shape
+    dev = logits.device
+    out = {
+        "topk_idx": torch.empty((t, top_k), dtype=torch.int32, device=dev),
+        "gates": torch.empty((t, top_k), dtype=torch.float32, device=dev),
+        "counts": torch.empty((e,), dtype=torch.int32, device=dev),
+        "offsets": torch.empty((e + 1,), dtype=torch.int32, device=dev),
+        "perm": torch.empty((t * top_k,), dtype=torch.int32, device=dev),
+        "inv": torch.empty((t, top_k), dtype=torch.int32, device=dev),
+    }
+    _check(lib.dsmoe_route(_p(logits), _p(bias), t, e, n_groups, groups_kept, top_k,
+                           _p(out["topk_idx"]), _p(out["gates"]), _p(out["counts"]), _p(out["offsets"]),
+                           _p(out["perm"]), _p(out["inv"]), _stream()), "dsmoe_route")
+    return out
+
+
+def fp8_grouped_gemm(a: torch.Tensor, a_scale: torch.Tensor, offsets: torch.Tensor, w: torch.Tensor,
+                     w_scale: torch.Tensor, out_dtype=torch.bfloat16, a_rows: Optional[torch.Tensor] = None,
+                     m_total: Optional[int] = None, c: Optional[torch.Tensor] = None):
+    """Grouped block-scaled FP8 GEMM (see dsmoe_fp8_grouped_gemm).
+
+    a uint8 [*][K], a_scale f32 [*][K/128], offsets int32 [G+1] (device),
+    w uint8 [G][N][K], w_scale f32 [G][N/128][K/128]; a_rows int32 [M_total]
+    or None.  m_total defaults to len(a_rows) or a.shape[0].
+    """
+    _dev(a, torch.uint8, "a")
+    _dev(a_scale, torch.float32, "a_scale")
+    _dev(offsets, torch.int32, "offsets")
+    if w.dim() == 2:
+        w = w.unsqueeze(0)
+        w_scale = w_scale.unsqueeze(0)
+    _dev(w, torch.uint8, "w")
+    _dev(w_scale, torch.float32, "w_scale")
+    if a_rows is not None:
+        _dev(a_rows, torch.int32, "a_rows")
+    g, n, k = w.shape
+    if offsets.numel() != g + 1:
+        raise ValueError("offsets must have G+1 entries")
+    if m_total is None:
+        m_total = a_rows.numel() if a_rows is not None else a.shape[0]
+    if c is None:
+        c = torch.empty((m_total, n), dtype=out_dtype, device=a.device)
+    _dev(c, c.dtype, "c")
+    _check(lib.dsmoe_fp8_grouped_gemm(_p(a), _p(a_scale), _p(a_rows), _p(offsets), g, m_total, _p(w),
+                                      _p(w_scale), n, k, _p(c), _dtype_code(c.dtype), _stream()),
+           "dsmoe_fp8_grouped_gemm")
+    return c
+
+
+@dataclasses.dataclass(frozen=True)
+class MoEDesc:
+    H: int
+    I: int
+    E: int
+    G: int
+    Mg: int
+    K: int
+    n_shared: int = 1
+
+    def _c(self):
+        return _Desc(self.H, self.I, self.E, self.G, self.Mg, self.K, self.n_shared)
+
+
+@dataclasses.dataclass
+class MoEWeights:
+    """Quantised layer weights on the device (see dsmoe_moe_weights)."""
+    w13: torch.Tensor
+    s13: torch.Tensor
+    w2: torch.Tensor
+    s2: torch.Tensor
+    w13_sh: Optional[torch.Tensor]
+    s13_sh: Optional[torch.Tensor]
+    w2_sh: Optional[torch.Tensor]
+    s2_sh: Optional[torch.Tensor]
+    router_w: torch.Tensor
+
+    def _c(self):
+        return _Weights(*[None if t is None else t.data_ptr() for t in (
+            self.w13, self.s13, self.w2, self.s2, self.w13_sh, self.s13_sh, self.w2_sh, self.s2_sh,
+            self.router_w)])
+
+
+def quantize_layer_weights(w13: torch.Tensor, w2: torch.Tensor, router_w: torch.Tensor,
+                           w13_sh: Optional[torch.Tensor] = None,
+                           w2_sh: Optional[torch.Tensor] = None) -> MoEWeights:
+    """Quantise bf16 expert weights with dsmoe_quant_w_128x128."""
+    q13, s13 = quant_w_128x128(w13)
+    q2, s2 = quant_w_128x128(w2)
+    q13s = s13s = q2s = s2s = None
+    if w13_sh is not None:
+        q13s, s13s = quant_w_128x128(w13_sh)
+        q2s, s2s = quant_w_128x128(w2_sh)
+    return MoEWeights(q13, s13, q2, s2, q13s, s13s, q2s, s2s, router_w)
+
+
+def moe_workspace_bytes(desc: MoEDesc, T: int) -> int:
+    d = desc._c()
+    return int(lib.dsmoe_moe_workspace_bytes(ctypes.byref(d), T))
+
+
+def moe_forward(desc: MoEDesc, weights: MoEWeights, bias: torch.Tensor, x: torch.Tensor,
+                out_dtype=torch.bfloat16, y: Optional[torch.Tensor] = None,
+                counts: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                debug: bool = False, stage_events=None):
+    """The layer forward (dsmoe_moe_forward).  Returns (y, counts, dbg) where
+    dbg is a dict of intermediates when debug=True, else None.
+    stage_events: optional sequence of STAGE_EVENTS raw hipEvent_t handles
+    (ints) recorded around the stages (see dsmoe_moe_debug)."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(bias, torch.float32, "bias")
+    _dev(weights.router_w, torch.bfloat16, "router_w")
+    T = x.shape[0]
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, desc.H), dtype=out_dtype, device=dev)
+    if counts is None:
+        counts = torch.empty((desc.E,), dtype=torch.int32, device=dev)
+    need = moe_workspace_bytes(desc, T)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    dbg = None
+    dbg_c = None
+    if debug:
+        dbg = {
+            "qx": torch.empty((T, desc.H), dtype=torch.uint8, device=dev),
+            "sx": torch.empty((T, desc.H // 128), dtype=torch.float32, device=dev),
+            "logits": torch.empty((T, desc.E), dtype=torch.float32, device=dev),
+            "topk_idx": torch.empty((T, desc.K), dtype=torch.int32, device=dev),
+            "gates": torch.empty((T, desc.K), dtype=torch.float32, device=dev),
+            "offsets": torch.empty((desc.E + 1,), dtype=torch.int32, device=dev),
+            "perm": torch.empty((T * desc.K,), dtype=torch.int32, device=dev),
+            "inv": torch.empty((T, desc.K), dtype=torch.int32, device=dev),
+        }
+        dbg_c = _Debug(*[dbg[n].data_ptr() for n in ("qx", "sx", "logits", "topk_idx", "gates",
+                                                      "offsets", "perm", "inv")])
+    if stage_events is not None:
+        if len(stage_events) != STAGE_EVENTS:
+            raise ValueError(f"stage_events needs {STAGE_EVENTS} handles")
+        arr = (_vp * STAGE_EVENTS)(*stage_events)
+        if dbg_c is None:
+            dbg_c = _Debug()
+        dbg_c.stage_events = ctypes.cast(arr, ctypes.POINTER(_vp))
+        dbg_c._keep = arr
+    d = desc._c()
+    wc = weights._c()
+    _check(lib.dsmoe_moe_forward(ctypes.byref(d), ctypes.byref(wc), _p(bias), _p(x), T, _p(y),
+                                 _dtype_code(y.dtype), _p(counts), _p(workspace), workspace.numel(),
+                                 ctypes.byref(dbg_c) if dbg_c is not None else None, _stream()),
+           "dsmoe_moe_forward")
+    return y, counts, dbg
+
+
+def update_bias(bias: torch.Tensor, counts: torch.Tensor, T: int, K: int, gamma: float = 0.001):
+    """In-place aux-loss-free bias update (dsmoe_update_bias)."""
+    _dev(bias, torch.float32, "bias")
+    _dev(counts, torch.int32, "counts")
+    _check(lib.dsmoe_update_bias(_p(bias), _p(counts), bias.numel(), T, K, float(gamma), _stream()),
+           "dsmoe_update_bias")
+    return bias

@@ -1,0 +1,384 @@
+// The extern "C" boundary: host-side validation, workspace layout and the
+// orchestration of the layer forward.  Nothing here allocates device memory;
+// every call validates all arguments before it enqueues anything.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "dsmoe.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647LL;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+dsmoe_status launch_status(hipError_t e) { return e == hipSuccess ? DSMOE_OK : DSMOE_ERR_LAUNCH; }
+
+// Device check, cached per device ordinal (idempotent).
+std::atomic<int> g_dev_ok[64];
+
+dsmoe_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DSMOE_ERR_DEVICE;
+  if (dev < 64) {
+    const int v = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (v == 1) return DSMOE_OK;
+    if (v == 2) return DSMOE_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DSMOE_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? DSMOE_OK : DSMOE_ERR_DEVICE;
+}
+
+bool valid_dtype(int t) { return t == DSMOE_BF16 || t == DSMOE_F32; }
+
+dsmoe_status check_routing_shape(int64_t T, int32_t E, int32_t G, int32_t Mg, int32_t K) {
+  if (T < 0) return DSMOE_ERR_SHAPE;
+  if (E < 1 || E > DSMOE_MAX_EXPERTS) return DSMOE_ERR_SHAPE;
+  if (G < 1 || G > DSMOE_MAX_GROUPS || E % G != 0) return DSMOE_ERR_SHAPE;
+  if (Mg < 1 || Mg > G) return DSMOE_ERR_SHAPE;
+  if (K < 1 || K > DSMOE_MAX_TOPK || static_cast<int64_t>(K) > static_cast<int64_t>(Mg) * (E / G))
+    return DSMOE_ERR_SHAPE;
+  if (T * (K + 1) > kI32Max) return DSMOE_ERR_SHAPE;
+  return DSMOE_OK;
+}
+
+// Workspace layout of dsmoe_moe_forward (every region 256-byte aligned).
+struct Layout {
+  size_t qx, sx, logits, topk, gates, offsets, offsets_ext, perm, inv, row_gate, qa, sa, o, total;
+};
+
+Layout layout_for(const dsmoe_moe_desc& d, int64_t T) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  const size_t TK = static_cast<size_t>(T) * d.K;
+  const size_t rows1 = TK + (d.n_shared ? static_cast<size_t>(T) : 0);
+  L.qx = take(static_cast<size_t>(T) * d.H);
+  L.sx = take(static_cast<size_t>(T) * (d.H / 128) * 4);
+  L.logits = take(static_cast<size_t>(T) * d.E * 4);
+  L.topk = take(TK * 4);
+  L.gates = take(TK * 4);
+  L.offsets = take((static_cast<size_t>(d.E) + 1) * 4);
+  L.offsets_ext = take((static_cast<size_t>(d.E) + 2) * 4);
+  L.perm = take(rows1 * 4);
+  L.inv = take(TK * 4);
+  L.row_gate = take(TK * 4);
+  L.qa = take(rows1 * d.I);
+  L.sa = take(rows1 * (d.I / 128) * 4);
+  L.o = take(TK * d.H * 4);
+  L.total = off;
+  return L;
+}
+
+dsmoe_status check_desc(const dsmoe_moe_desc* d, int64_t T) {
+  if (!d) return DSMOE_ERR_NULL;
+  if (d->H <= 0 || d->I <= 0 || d->H % 128 || d->I % 128) return DSMOE_ERR_SHAPE;
+  if (d->n_shared != 0 && d->n_shared != 1) return DSMOE_ERR_SHAPE;
+  const dsmoe_status s = check_routing_shape(T, d->E, d->G, d->Mg, d->K);
+  if (s != DSMOE_OK) return s;
+  if (T * d->H > (1LL << 40) || static_cast<int64_t>(d->E) * d->H > (1LL << 40)) return DSMOE_ERR_SHAPE;
+  return DSMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsmoe_status_str(int status) {
+  switch (status) {
+    case DSMOE_OK: return "DSMOE_OK";
+    case DSMOE_ERR_NULL: return "DSMOE_ERR_NULL";
+    case DSMOE_ERR_SHAPE: return "DSMOE_ERR_SHAPE";
+    case DSMOE_ERR_ALIGN: return "DSMOE_ERR_ALIGN";
+    case DSMOE_ERR_DTYPE: return "DSMOE_ERR_DTYPE";
+    case DSMOE_ERR_WORKSPACE: return "DSMOE_ERR_WORKSPACE";
+    case DSMOE_ERR_DEVICE: return "DSMOE_ERR_DEVICE";
+    case DSMOE_ERR_LAUNCH: return "DSMOE_ERR_LAUNCH";
+    default: return "DSMOE_ERR_UNKNOWN";
+  }
+}
+
+int dsmoe_abi_version(void) { return 1; }
+
+dsmoe_status dsmoe_quant_act_1x128(const void* x, int xt, int64_t rows, int64_t cols, uint8_t* q,
+                                   float* scale, void* stream) {
+  if (!valid_dtype(xt)) return DSMOE_ERR_DTYPE;
+  if (rows < 0 || cols <= 0 || cols % 128) return DSMOE_ERR_SHAPE;
+  if (rows * (cols / 128) * 16 / 256 >= kI32Max) return DSMOE_ERR_SHAPE;
+  if (rows == 0) return DSMOE_OK;
+  if (!x || !q || !scale) return DSMOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  return launch_status(dsmoe::launch_quant_act(x, xt == DSMOE_F32, rows, cols, q, scale,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+dsmoe_status dsmoe_quant_w_128x128(const void* w, int wt, int64_t n_mats, int64_t N, int64_t K,
+                                   uint8_t* q, float* scale, void* stream) {
+  if (!valid_dtype(wt)) return DSMOE_ERR_DTYPE;
+  if (n_mats < 0 || N <= 0 || K <= 0 || N % 128 || K % 128) return DSMOE_ERR_SHAPE;
+  if (n_mats * (N / 128) * (K / 128) >= kI32Max) return DSMOE_ERR_SHAPE;
+  if (n_mats == 0) return DSMOE_OK;
+  if (!w || !q || !scale) return DSMOE_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scale, 4)) return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  return launch_status(dsmoe::launch_quant_w(w, wt == DSMOE_F32, n_mats, N, K, q, scale,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+dsmoe_status dsmoe_route(const float* logits, const float* bias, int64_t T, int32_t E, int32_t G,
+                         int32_t Mg, int32_t K, int32_t* topk_idx, float* gates, int32_t* counts,
+                         int32_t* offsets, int32_t* perm, int32_t* inv, void* stream) {
+  dsmoe_status s = check_routing_shape(T, E, G, Mg, K);
+  if (s != DSMOE_OK) return s;
+  if (!bias || !counts || !offsets) return DSMOE_ERR_NULL;
+  if (T > 0 && (!logits || !topk_idx || !gates || !perm || !inv)) return DSMOE_ERR_NULL;
+  const void* ptrs[] = {logits, bias, topk_idx, gates, counts, offsets, perm, inv};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 4)) return DSMOE_ERR_ALIGN;
+  s = check_device();
+  if (s != DSMOE_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = dsmoe::launch_route_select(logits, bias, T, E, G, Mg, K, topk_idx, gates, counts, st);
+  if (e != hipSuccess) return DSMOE_ERR_LAUNCH;
+  e = dsmoe::launch_permute(topk_idx, gates, T, E, K, counts, offsets, perm, inv, nullptr, nullptr, st);
+  return launch_status(e);
+}
+
+dsmoe_status dsmoe_fp8_grouped_gemm(const uint8_t* a, const float* a_scale,
+                                    const int32_t* a_rows, const int32_t* offsets, int32_t G,
+                                    int64_t M_total, const uint8_t* w, const float* w_scale,
+                                    int64_t N, int64_t K, void* c, int ct, void* stream) {
+  if (!valid_dtype(ct)) return DSMOE_ERR_DTYPE;
+  if (G < 1 || M_total < 0 || N <= 0 || K <= 0 || N % 128 || K % 128) return DSMOE_ERR_SHAPE;
+  if (M_total > kI32Max || G > kI32Max / 2) return DSMOE_ERR_SHAPE;
+  if (((M_total + 127) / 128 + G) * (N / 128) >= kI32Max) return DSMOE_ERR_SHAPE;
+  if (M_total == 0) return DSMOE_OK;
+  if (!a || !a_scale || !offsets || !w || !w_scale || !c) return DSMOE_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(c, 16) || !aligned(a_scale, 4) ||
+      !aligned(w_scale, 4) || !aligned(offsets, 4) || (a_rows && !aligned(a_rows, 4)))
+    return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  dsmoe::GemmProblem p{};
+  p.a = a;
+  p.a_scale = a_scale;
+  p.a_rows = a_rows;
+  p.offsets = offsets;
+  p.G = G;
+  p.M_total = M_total;
+  p.w = w;
+  p.w_scale = w_scale;
+  p.N = N;
+  p.K = K;
+  p.c = c;
+  p.c_f32 = ct == DSMOE_F32;
+  p.epi = dsmoe::Epilogue::kStore;
+  p.row_limit = M_total;
+  return launch_status(dsmoe::launch_grouped_gemm(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t dsmoe_moe_workspace_bytes(const dsmoe_moe_desc* d, int64_t T) {
+  if (check_desc(d, T) != DSMOE_OK) return 0;
+  return layout_for(*d, T).total;
+}
+
+dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights* w,
+                               const float* bias, const void* x, int64_t T, void* y, int yt,
+                               int32_t* counts_out, void* workspace, size_t ws_bytes,
+                               const dsmoe_moe_debug* dbg, void* stream) {
+  dsmoe_status s = check_desc(d, T);
+  if (s != DSMOE_OK) return s;
+  if (!valid_dtype(yt)) return DSMOE_ERR_DTYPE;
+  if (!w || !bias || !counts_out) return DSMOE_ERR_NULL;
+  if (!w->w13 || !w->s13 || !w->w2 || !w->s2 || !w->router_w) return DSMOE_ERR_NULL;
+  if (d->n_shared && (!w->w13_sh || !w->s13_sh || !w->w2_sh || !w->s2_sh)) return DSMOE_ERR_NULL;
+  if (T > 0 && (!x || !y)) return DSMOE_ERR_NULL;
+  const Layout L = layout_for(*d, T);
+  if (T > 0 && !workspace) return DSMOE_ERR_WORKSPACE;
+  if (ws_bytes < L.total) return DSMOE_ERR_WORKSPACE;
+  if ((x && !aligned(x, 16)) || (y && !aligned(y, 16)) || !aligned(w->w13, 16) ||
+      !aligned(w->w2, 16) || !aligned(w->router_w, 16) || !aligned(w->s13, 4) ||
+      !aligned(w->s2, 4) || !aligned(bias, 4) || !aligned(counts_out, 4) ||
+      (workspace && !aligned(workspace, 256)))
+    return DSMOE_ERR_ALIGN;
+  if (d->n_shared && (!aligned(w->w13_sh, 16) || !aligned(w->w2_sh, 16) ||
+                      !aligned(w->s13_sh, 4) || !aligned(w->s2_sh, 4)))
+    return DSMOE_ERR_ALIGN;
+  if (dbg) {
+    const void* dp[] = {dbg->qx, dbg->sx, dbg->logits, dbg->topk_idx, dbg->gates,
+                        dbg->offsets, dbg->perm, dbg->inv};
+    for (const void* p : dp)
+      if (p && !aligned(p, 4)) return DSMOE_ERR_ALIGN;
+  }
+  s = check_device();
+  if (s != DSMOE_OK) return s;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t H = d->H, I = d->I;
+  const int32_t E = d->E, K = d->K;
+  const bool f32out = yt == DSMOE_F32;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* qx = ws + L.qx;
+  float* sx = reinterpret_cast<float*>(ws + L.sx);
+  float* logits = reinterpret_cast<float*>(ws + L.logits);
+  int32_t* topk = reinterpret_cast<int32_t*>(ws + L.topk);
+  float* gates = reinterpret_cast<float*>(ws + L.gates);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* offsets_ext = reinterpret_cast<int32_t*>(ws + L.offsets_ext);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  float* row_gate = reinterpret_cast<float*>(ws + L.row_gate);
+  uint8_t* qa = ws + L.qa;
+  float* sa = reinterpret_cast<float*>(ws + L.sa);
+  void* o = ws + L.o;
+
+  hipError_t e;
+#define DSMOE_TRY(expr)              \
+  do {                               \
+    e = (expr);                      \
+    if (e != hipSuccess) return DSMOE_ERR_LAUNCH; \
+  } while (0)
+
+  if (T == 0) {
+    DSMOE_TRY(dsmoe::launch_route_select(nullptr, bias, 0, E, d->G, d->Mg, K, nullptr, nullptr,
+                                         counts_out, st));
+    return DSMOE_OK;
+  }
+  void* const* ev = dbg ? dbg->stage_events : nullptr;
+#define DSMOE_MARK(i) \
+  if (ev) DSMOE_TRY(hipEventRecord(static_cast<hipEvent_t>(ev[(i)]), st))
+
+  DSMOE_MARK(0);
+
+  // a1: 1x128 quantisation of x
+  DSMOE_TRY(dsmoe::launch_quant_act(x, false, T, H, qx, sx, st));
+  DSMOE_MARK(1);
+  // a3: router logits (bf16 MFMA, FP32 accumulation)
+  DSMOE_TRY(dsmoe::launch_router_logits(static_cast<const uint16_t*>(x),
+                                        static_cast<const uint16_t*>(w->router_w), T, H, E,
+                                        logits, st));
+  DSMOE_MARK(2);
+  // a4: routing
+  DSMOE_TRY(dsmoe::launch_route_select(logits, bias, T, E, d->G, d->Mg, K, topk, gates,
+                                       counts_out, st));
+  DSMOE_MARK(3);
+  // a5: counts -> offsets, permutation, inverse, per-row gates; shared rows
+  DSMOE_TRY(dsmoe::launch_permute(topk, gates, T, E, K, counts_out, offsets, perm, inv, row_gate,
+                                  d->n_shared ? offsets_ext : nullptr, st));
+  DSMOE_MARK(4);
+
+  // a6 + a7 (+ a9 first half): gate/up GEMM with SwiGLU and 1x128 requant
+  dsmoe::GemmProblem g1{};
+  g1.a = qx;
+  g1.a_scale = sx;
+  g1.a_rows = perm;
+  g1.offsets = d->n_shared ? offsets_ext : offsets;
+  g1.G = E + (d->n_shared ? 1 : 0);
+  g1.M_total = T * K + (d->n_shared ? T : 0);
+  g1.w = w->w13;
+  g1.w_scale = w->s13;
+  g1.w_last = d->n_shared ? w->w13_sh : nullptr;
+  g1.w_scale_last = d->n_shared ? w->s13_sh : nullptr;
+  g1.N = 2 * I;
+  g1.K = H;
+  g1.c = qa;
+  g1.c_scale = sa;
+  g1.epi = dsmoe::Epilogue::kSwiGLUQuant;
+  g1.row_limit = g1.M_total;
+  DSMOE_TRY(dsmoe::launch_grouped_gemm(g1, st));
+  DSMOE_MARK(5);
+
+  // a8: routed down projection, scaled by the gate
+  dsmoe::GemmProblem g2{};
+  g2.a = qa;
+  g2.a_scale = sa;
+  g2.a_rows = nullptr;
+  g2.offsets = offsets;
+  g2.G = E;
+  g2.M_total = T * K;
+  g2.w = w->w2;
+  g2.w_scale = w->s2;
+  g2.N = H;
+  g2.K = I;
+  g2.c = o;
+  g2.c_f32 = f32out;
+  g2.row_gate = row_gate;
+  g2.epi = dsmoe::Epilogue::kGateStore;
+  g2.row_limit = g2.M_total;
+  DSMOE_TRY(dsmoe::launch_grouped_gemm(g2, st));
+  DSMOE_MARK(6);
+
+  if (d->n_shared) {
+    // a9 (down projection of the shared expert) + a10 combine in its epilogue
+    dsmoe::GemmProblem g3{};
+    g3.a = qa;
+    g3.a_scale = sa;
+    g3.a_rows = nullptr;
+    g3.offsets = offsets_ext + E;  // {T*K, T*K + T}
+    g3.G = 1;
+    g3.M_total = T;
+    g3.w = w->w2_sh;
+    g3.w_scale = w->s2_sh;
+    g3.N = H;
+    g3.K = I;
+    g3.c = y;
+    g3.c_f32 = f32out;
+    g3.o_routed = o;
+    g3.inv = inv;
+    g3.topk = K;
+    g3.row_base = T * K;
+    g3.epi = dsmoe::Epilogue::kCombine;
+    g3.row_limit = T * K + T;
+    DSMOE_TRY(dsmoe::launch_grouped_gemm(g3, st));
+  } else {
+    DSMOE_TRY(dsmoe::launch_combine(o, inv, T, K, H, y, f32out, st));
+  }
+  DSMOE_MARK(7);
+#undef DSMOE_MARK
+
+  if (dbg) {
+    const size_t TK = static_cast<size_t>(T) * K;
+    struct Cp { void* dst; const void* src; size_t n; } cps[] = {
+        {dbg->qx, qx, static_cast<size_t>(T) * H},
+        {dbg->sx, sx, static_cast<size_t>(T) * (H / 128) * 4},
+        {dbg->logits, logits, static_cast<size_t>(T) * E * 4},
+        {dbg->topk_idx, topk, TK * 4},
+        {dbg->gates, gates, TK * 4},
+        {dbg->offsets, offsets, (static_cast<size_t>(E) + 1) * 4},
+        {dbg->perm, perm, TK * 4},
+        {dbg->inv, inv, TK * 4},
+    };
+    for (const Cp& c : cps)
+      if (c.dst) DSMOE_TRY(hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, st));
+  }
+#undef DSMOE_TRY
+  return DSMOE_OK;
+}
+
+dsmoe_status dsmoe_update_bias(float* bias, const int32_t* counts, int32_t E, int64_t T,
+                               int32_t K, float gamma, void* stream) {
+  if (E < 1 || E > DSMOE_MAX_EXPERTS || T < 0 || K < 1) return DSMOE_ERR_SHAPE;
+  if (!bias || !counts) return DSMOE_ERR_NULL;
+  if (!aligned(bias, 4) || !aligned(counts, 4)) return DSMOE_ERR_ALIGN;
+  const dsmoe_status s = check_device();
+  if (s != DSMOE_OK) return s;
+  return launch_status(dsmoe::launch_update_bias(bias, counts, E, T, K, gamma,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Device-side building blocks shared by the dsmoe kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsmoe {
+
+constexpr int kWave = 64;
+constexpr int kTile = 128;  // quantisation tile / promotion interval
+
+// ---------------------------------------------------------------------------
+// bf16 <-> f32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// OCP E4M3FN encoder: round to nearest, ties to even, saturate at +-448,
+// sign of zero kept.  Integer-only apart from the exact scaling of the
+// subnormal range, so it is bit-exact by construction:
+//   |v| >= 448           -> 0x7E
+//   |v| <  2^-6          -> n = rne(|v| * 2^9), code n (n = 8 is 0x08)
+//   otherwise            -> keep 3 mantissa bits, round on the 20 dropped
+//                           bits; a carry out of the mantissa increments the
+//                           exponent field through the plain addition.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t bits = __float_as_uint(v);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t mag = bits & 0x7FFFFFFFu;
+  if (mag >= 0x43E00000u) return sign | 0x7Eu;            // >= 448 (and Inf/NaN)
+  if (mag < 0x3C800000u) {                                // < 2^-6
+    const float t = __uint_as_float(mag) * 512.0f;        // exact power-of-2 scaling
+    return sign | static_cast<uint32_t>(__builtin_rintf(t));
+  }
+  const uint32_t e = (mag >> 23) - 127u + 7u;             // 1..15
+  const uint32_t m = mag & 0x7FFFFFu;
+  uint32_t keep = m >> 20;
+  const uint32_t rest = m & 0xFFFFFu;
+  keep += (rest > 0x80000u) || (rest == 0x80000u && (keep & 1u));
+  return sign | ((e << 3) + keep);
+}
+
+// ---------------------------------------------------------------------------
+// Wave helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max_width(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, width));
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+}  // namespace dsmoe

@@ -1,0 +1,70 @@
+// Internal launchers of the dsmoe kernels.  Called by the C ABI layer after
+// it has validated every argument; each returns hipSuccess or the launch
+// error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsmoe {
+
+// quant.hip
+hipError_t launch_quant_act(const void* x, bool x_f32, int64_t rows, int64_t cols, uint8_t* q,
+                            float* scale, hipStream_t s);
+hipError_t launch_quant_w(const void* w, bool w_f32, int64_t n_mats, int64_t n, int64_t k,
+                          uint8_t* q, float* scale, hipStream_t s);
+
+// route.hip
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, int64_t T, int64_t H,
+                                int32_t E, float* logits, hipStream_t s);
+// topk/gates + per-expert counts (counts are zeroed first by the launcher)
+hipError_t launch_route_select(const float* logits, const float* bias, int64_t T, int32_t E,
+                               int32_t G, int32_t Mg, int32_t K, int32_t* topk_idx,
+                               float* gates, int32_t* counts, hipStream_t s);
+// offsets from counts; perm/inv (and, when given, per-row gates and the
+// identity extension of perm for `extra_rows` trailing rows)
+hipError_t launch_permute(const int32_t* topk_idx, const float* gates, int64_t T, int32_t E,
+                          int32_t K, const int32_t* counts, int32_t* offsets, int32_t* perm,
+                          int32_t* inv, float* row_gate, int32_t* offsets_ext,
+                          hipStream_t s);
+hipError_t launch_update_bias(float* bias, const int32_t* counts, int32_t E, int64_t T,
+                              int32_t K, float gamma, hipStream_t s);
+
+// gemm.hip
+enum class Epilogue : int {
+  kStore = 0,      // c[r][n] = acc (bf16 or f32)
+  kGateStore = 1,  // c[r][n] = acc * row_gate[r]
+  kSwiGLUQuant = 2,// h = [gate | up] -> a = silu(gate) * up -> 1x128 FP8 codes + scales
+  kCombine = 3,    // y[t][n] = acc + sum_k o[inv[t][k]][n]  (shared expert rows)
+};
+
+struct GemmProblem {
+  const uint8_t* a;          // [*][K] codes
+  const float* a_scale;      // [*][K/128]
+  const int32_t* a_rows;     // [M_total] or null
+  const int32_t* offsets;    // [G+1] device
+  int32_t G;
+  int64_t M_total;           // upper bound on the rows the groups hold (grid sizing)
+  const uint8_t* w;          // [G][N][K] codes (or G-1 matrices + w_last)
+  const float* w_scale;      // [G][N/128][K/128]
+  const uint8_t* w_last;     // when non-null: group G-1 uses these
+  const float* w_scale_last;
+  int64_t N, K;              // N = columns of W (for SwiGLU: 2I)
+  void* c;                   // output
+  bool c_f32;
+  // epilogue extras
+  Epilogue epi;
+  const float* row_gate;     // kGateStore
+  float* c_scale;            // kSwiGLUQuant: [M_total][N/2/128]
+  const void* o_routed;      // kCombine: [T*K][N], same dtype as c
+  const int32_t* inv;        // kCombine: [T][K]
+  int32_t topk;              // kCombine
+  int64_t row_base;          // kCombine: output row r is token r - row_base
+  int64_t row_limit;         // rows >= row_limit are never read or written
+};
+
+hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t s);
+hipError_t launch_combine(const void* o, const int32_t* inv, int64_t T, int32_t K, int64_t H,
+                          void* y, bool f32, hipStream_t s);
+
+}  // namespace dsmoe

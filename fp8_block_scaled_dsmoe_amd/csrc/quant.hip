@@ -1,0 +1,132 @@
+// Fine-grained online FP8 quantisation (1x128 activation tiles, 128x128
+// weight blocks), per V3 notes (xutianle.me "DeepSeek-V3 技术报告" walk-through)
+// §6.1: one scale per token per 128 channels for activations, one per
+// 128x128 block for weights, computed from the tensor itself.
+//
+// s = fl32(amax / 448) (IEEE division; 1 for an all-zero tile),
+// q = E4M3(fl32(x / s)) (IEEE division, nearest-even, saturating).
+// Both kernels are HBM-streaming: every input byte is read once and every
+// code written once, with 16-byte accesses.
+#include "common.h"
+#include "kernels.h"
+
+namespace dsmoe {
+namespace {
+
+template <bool kF32>
+__device__ __forceinline__ void load8(const void* base, int64_t idx, float (&v)[8]) {
+  if constexpr (kF32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    const float4 a = p[0];
+    const float4 b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+}
+
+__device__ __forceinline__ uint2 encode8(const float (&v)[8], float s) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= e4m3_encode(v[i] / s) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= e4m3_encode(v[4 + i] / s) << (8 * i);
+  return make_uint2(lo, hi);
+}
+
+__device__ __forceinline__ float scale_from_amax(float amax) {
+  return amax == 0.0f ? 1.0f : amax / 448.0f;
+}
+
+// 16 lanes per 1x128 tile, 8 elements per lane.
+template <bool kF32>
+__global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__ x, int64_t rows,
+                                                        int64_t cols, uint8_t* __restrict__ q,
+                                                        float* __restrict__ scale) {
+  const int64_t tiles_per_row = cols / kTile;
+  const int64_t tile = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 4;
+  const int sub = threadIdx.x & 15;
+  if (tile >= rows * tiles_per_row) return;  // all 16 lanes of a tile leave together
+  const int64_t r = tile / tiles_per_row;
+  const int64_t j = tile - r * tiles_per_row;
+  const int64_t idx = r * cols + j * kTile + sub * 8;
+  float v[8];
+  load8<kF32>(x, idx, v);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = wave_max_width(amax, 16);
+  const float s = scale_from_amax(amax);
+  *reinterpret_cast<uint2*>(q + idx) = encode8(v, s);
+  if (sub == 0) scale[r * tiles_per_row + j] = s;
+}
+
+// One 256-thread block per 128x128 block: lane column segment t%16 (8
+// elements), rows t/16 + 16*i.
+template <bool kF32>
+__global__ __launch_bounds__(256) void quant_w_kernel(const void* __restrict__ w, int64_t n,
+                                                      int64_t k, uint8_t* __restrict__ q,
+                                                      float* __restrict__ scale) {
+  __shared__ float red[4];
+  const int64_t nb = n / kTile, kb = k / kTile;
+  const int64_t blk = blockIdx.x;
+  const int64_t mat = blk / (nb * kb);
+  const int64_t rem = blk - mat * nb * kb;
+  const int64_t bi = rem / kb, bj = rem - bi * kb;
+  const int seg = threadIdx.x & 15;
+  const int r0 = threadIdx.x >> 4;
+  const int64_t base = mat * n * k + (bi * kTile) * k + bj * kTile + seg * 8;
+
+  float v[8][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    load8<kF32>(w, base + static_cast<int64_t>(r0 + 16 * i) * k, v[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
+  }
+  amax = wave_max_width(amax, kWave);
+  if (lane_id() == 0) red[threadIdx.x / kWave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = scale_from_amax(amax);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint2*>(q + base + static_cast<int64_t>(r0 + 16 * i) * k) = encode8(v[i], s);
+  if (threadIdx.x == 0) scale[mat * nb * kb + bi * kb + bj] = s;
+}
+
+}  // namespace
+
+hipError_t launch_quant_act(const void* x, bool x_f32, int64_t rows, int64_t cols, uint8_t* q,
+                            float* scale, hipStream_t s) {
+  const int64_t threads = rows * (cols / kTile) * 16;
+  if (threads == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  if (x_f32)
+    quant_act_kernel<true><<<grid, 256, 0, s>>>(x, rows, cols, q, scale);
+  else
+    quant_act_kernel<false><<<grid, 256, 0, s>>>(x, rows, cols, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_w(const void* w, bool w_f32, int64_t n_mats, int64_t n, int64_t k,
+                          uint8_t* q, float* scale, hipStream_t s) {
+  const int64_t blocks = n_mats * (n / kTile) * (k / kTile);
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  if (w_f32)
+    quant_w_kernel<true><<<grid, 256, 0, s>>>(w, n, k, q, scale);
+  else
+    quant_w_kernel<false><<<grid, 256, 0, s>>>(w, n, k, q, scale);
+  return hipGetLastError();
+}
+
+}  // namespace dsmoe

@@ -1,0 +1,390 @@
+// Router logits, auxiliary-loss-free group-limited top-K routing, the token
+// permute and the bias update.
+//
+// Sources (V3 notes = xutianle.me "DeepSeek-V3 技术报告" walk-through):
+//  * V3 notes §4: choose the top-K experts on s + b, weight the chosen ones by
+//    the raw affinity s; after every step lower the bias of overloaded experts
+//    and raise that of underloaded ones (§4.1: speed gamma = 0.001).
+//  * V3 notes §4.2 / 51itzy.com infra answer (routing paragraph): a token may
+//    only reach experts on a limited number of nodes (4 of 8); no dropping.
+//  * V3 notes §6: the router is one of the cheap / sensitive modules kept in
+//    higher precision, so its GEMM is bf16 x bf16 with FP32 accumulation.
+//
+// Readings taken where the page's formulas were lost: sigmoid affinity
+// evaluated in float64 and rounded once to float32; key = fl32(s + b); a
+// group scores by the float32 sum (largest first) of its ceil(K/Mg) largest
+// keys; ties go to the lower group / expert index; gates are s normalised
+// over the chosen experts (float32 sum in selection order).
+#include "common.h"
+#include "kernels.h"
+
+namespace dsmoe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Router logits z[T][E] = x[T][H] . Wr[E][H]^T on bf16 MFMA (16x16x32).
+// Block tile 64 tokens x 64 experts, K step 64, LDS double buffer with a
+// 16-byte-segment XOR swizzle; four waves, each 32 x 32 (2 x 2 MFMA tiles).
+// ---------------------------------------------------------------------------
+constexpr int RT = 64, RE = 64, RK = 64;  // RK bf16 = 128 bytes per row
+
+__device__ __forceinline__ int swz(int row, int seg) { return row * 128 + ((seg ^ (row & 7)) << 4); }
+
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ wr,
+                                                            int64_t T, int64_t H, int32_t E,
+                                                            float* __restrict__ z) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][RT * 128];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RT;
+  const int e0 = blockIdx.y * RE;
+
+  // global -> register loads: 2 x 16 bytes of x and of Wr per thread per step
+  const uint16_t* xsrc[2];
+  const uint16_t* wsrc[2];
+  int lrow[2], lseg[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + 256 * i;  // 0..511: 64 rows x 8 segments
+    lrow[i] = idx >> 3;
+    lseg[i] = idx & 7;
+    const int64_t tr = min<int64_t>(t0 + lrow[i], T - 1);
+    const int er = min(e0 + lrow[i], E - 1);
+    xsrc[i] = x + tr * H + lseg[i] * 8;
+    wsrc[i] = wr + static_cast<int64_t>(er) * H + lseg[i] * 8;
+  }
+  u32x4 xr[2], wrr[2];
+#define DSMOE_GLOAD(k0)                                                    \
+  do {                                                                     \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i) {                        \
+      xr[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + (k0));             \
+      wrr[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + (k0));            \
+    }                                                                      \
+  } while (0)
+#define DSMOE_SSTORE(bb)                                                   \
+  do {                                                                     \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i) {                        \
+      *reinterpret_cast<u32x4*>(&lds[(bb)][0][swz(lrow[i], lseg[i])]) = xr[i];  \
+      *reinterpret_cast<u32x4*>(&lds[(bb)][1][swz(lrow[i], lseg[i])]) = wrr[i]; \
+    }                                                                      \
+  } while (0)
+
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t steps = H / RK;
+  DSMOE_GLOAD(0);
+  DSMOE_SSTORE(0);
+  __syncthreads();
+  for (int64_t st = 0; st < steps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < steps) DSMOE_GLOAD((st + 1) * RK);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int seg = ks * 4 + (lane >> 4);
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = *reinterpret_cast<const bf16x8*>(&lds[buf][0][swz(wm * 32 + i * 16 + (lane & 15), seg)]);
+        bfr[i] = *reinterpret_cast<const bf16x8*>(&lds[buf][1][swz(wn * 32 + i * 16 + (lane & 15), seg)]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (st + 1 < steps) DSMOE_SSTORE(buf ^ 1);
+    __syncthreads();
+  }
+#undef DSMOE_GLOAD
+#undef DSMOE_SSTORE
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int e = e0 + wn * 32 + j * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
+        if (t < T && e < E) z[t * E + e] = acc[i][j][r];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Top-K selection: one wave per token.  Expert e lives in lane e % 64,
+// slot e / 64.  Ordering everywhere: value descending, index ascending.
+// ---------------------------------------------------------------------------
+struct Cand {
+  float v;
+  int i;      // index; -1 = no candidate
+  float pay;  // payload carried with the winner (the raw affinity s)
+};
+
+__device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
+  if (a.i < 0) return false;
+  if (b.i < 0) return true;
+  return a.v > b.v || (a.v == b.v && a.i < b.i);
+}
+
+__device__ __forceinline__ Cand wave_best(Cand c) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    Cand d;
+    d.v = __shfl_xor(c.v, o, 64);
+    d.i = __shfl_xor(c.i, o, 64);
+    d.pay = __shfl_xor(c.pay, o, 64);
+    if (better(d, c)) c = d;
+  }
+  return c;
+}
+
+template <int SLOTS>
+__global__ __launch_bounds__(256) void route_select_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int64_t T, int32_t E,
+    int32_t G, int32_t Mg, int32_t K, int32_t* __restrict__ topk_idx, float* __restrict__ gates,
+    int32_t* __restrict__ counts) {
+  extern __shared__ float key_lds[];  // [4 waves][E]
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int64_t t_raw = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const bool valid = t_raw < T;
+  const int64_t t = valid ? t_raw : T - 1;  // tail waves recompute the last token, write nothing
+  float* keys = key_lds + wave * E;
+
+  float s[SLOTS], key[SLOTS];
+  const float* zrow = logits + t * E;
+#pragma unroll
+  for (int j = 0; j < SLOTS; ++j) {
+    const int e = j * 64 + lane;
+    if (e < E) {
+      const double zd = static_cast<double>(zrow[e]);
+      s[j] = static_cast<float>(1.0 / (1.0 + exp(-zd)));
+      key[j] = s[j] + bias[e];
+      keys[e] = key[j];
+    } else {
+      s[j] = 0.f;
+      key[j] = 0.f;
+    }
+  }
+  __syncthreads();
+
+  // group scores: lane g < G sums the n_top largest keys of its group, found
+  // by repeated "next in order after the previous pick" scans
+  const int per_group = E / G;
+  const int n_top = (K + Mg - 1) / Mg;
+  Cand gs;
+  gs.i = -1;
+  gs.v = 0.f;
+  gs.pay = 0.f;
+  if (lane < G) {
+    float acc = 0.f;
+    float pv = 0.f;
+    int pi = -1;
+    for (int n = 0; n < n_top; ++n) {
+      float bv = 0.f;
+      int bi = -1;
+      for (int q = 0; q < per_group; ++q) {
+        const int e = lane * per_group + q;
+        const float v = keys[e];
+        const bool after = (pi < 0) || (v < pv) || (v == pv && e > pi);
+        if (after && (bi < 0 || v > bv)) {  // strict > keeps the lowest index on ties
+          bv = v;
+          bi = e;
+        }
+      }
+      acc = (n == 0) ? bv : acc + bv;
+      pv = bv;
+      pi = bi;
+    }
+    gs.v = acc;
+    gs.i = lane;
+  }
+
+  // keep the Mg best groups
+  uint64_t kept = 0;
+  for (int m = 0; m < Mg; ++m) {
+    Cand c = gs;
+    if (c.i >= 0 && ((kept >> c.i) & 1ull)) c.i = -1;
+    const Cand w = wave_best(c);
+    kept |= 1ull << w.i;
+  }
+
+  // choose K experts among the kept groups; lane k keeps the k-th choice and
+  // every lane forms the same float32 sum of s in selection order
+  uint32_t taken = 0;
+  int my_e = 0;
+  float my_s = 0.f;
+  float sum = 0.f;
+  for (int k = 0; k < K; ++k) {
+    Cand c;
+    c.i = -1;
+    c.v = 0.f;
+    c.pay = 0.f;
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+      const int e = j * 64 + lane;
+      if (e < E && !((taken >> j) & 1u) && ((kept >> (e / per_group)) & 1ull)) {
+        Cand d{key[j], e, s[j]};
+        if (better(d, c)) c = d;
+      }
+    }
+    const Cand w = wave_best(c);
+    if ((w.i & 63) == lane) taken |= 1u << (w.i >> 6);
+    if (lane == k) {
+      my_e = w.i;
+      my_s = w.pay;
+    }
+    sum = (k == 0) ? w.pay : sum + w.pay;
+  }
+
+  if (valid && lane < K) {
+    topk_idx[t * K + lane] = my_e;
+    gates[t * K + lane] = my_s / sum;
+    atomicAdd(&counts[my_e], 1);
+  }
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// offsets = exclusive scan of counts (one block of 1024 threads, E <= 1024);
+// optionally the extended table with one more group of `extra` rows.
+__global__ __launch_bounds__(1024) void offsets_kernel(const int32_t* __restrict__ counts,
+                                                       int32_t E, int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ offsets_ext,
+                                                       int64_t extra) {
+  __shared__ int32_t buf[1024];
+  const int tid = threadIdx.x;
+  int32_t v = tid < E ? counts[tid] : 0;
+  buf[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int32_t add = tid >= o ? buf[tid - o] : 0;
+    __syncthreads();
+    buf[tid] += add;
+    __syncthreads();
+  }
+  if (tid < E) {
+    offsets[tid + 1] = buf[tid];
+    if (offsets_ext) offsets_ext[tid + 1] = buf[tid];
+  }
+  if (tid == 0) {
+    offsets[0] = 0;
+    if (offsets_ext) {
+      offsets_ext[0] = 0;
+      offsets_ext[E + 1] = buf[E - 1] + static_cast<int32_t>(extra);
+    }
+  }
+}
+
+// Block e lists the (token, k) entries that chose expert e, in token order,
+// with a block-wide ballot prefix count.  Entry i = t*K + k.
+__global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ topk_idx,
+                                                   const float* __restrict__ gates, int64_t T,
+                                                   int32_t E, int32_t K,
+                                                   const int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ perm,
+                                                   int32_t* __restrict__ inv,
+                                                   float* __restrict__ row_gate,
+                                                   int32_t ext) {
+  __shared__ int32_t wave_cnt[4];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t n = T * K;
+  int32_t base = offsets[e];
+  for (int64_t i0 = 0; i0 < n; i0 += 256) {
+    const int64_t i = i0 + tid;
+    const bool match = i < n && topk_idx[i] == e;
+    const uint64_t bal = __ballot(match);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int wbase = 0;
+    for (int w = 0; w < wave; ++w) wbase += wave_cnt[w];
+    const int total = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+    if (match) {
+      const int32_t pos = base + wbase + before;
+      perm[pos] = static_cast<int32_t>(i / K);
+      inv[i] = pos;
+      if (row_gate) row_gate[pos] = gates[i];
+    }
+    base += total;
+    __syncthreads();
+  }
+  if (ext) {  // identity rows for the shared expert: perm[T*K + t] = t
+    for (int64_t t = static_cast<int64_t>(e) * 256 + tid; t < T; t += static_cast<int64_t>(E) * 256)
+      perm[n + t] = static_cast<int32_t>(t);
+  }
+}
+
+__global__ void update_bias_kernel(float* __restrict__ bias, const int32_t* __restrict__ counts,
+                                   int32_t E, int64_t T, int32_t K, float gamma) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const int64_t d = T * K - static_cast<int64_t>(E) * counts[e];
+  const float step = d > 0 ? gamma : (d < 0 ? -gamma : 0.0f);
+  bias[e] = bias[e] + step;
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, int64_t T, int64_t H,
+                                int32_t E, float* logits, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((T + RT - 1) / RT), static_cast<unsigned>((E + RE - 1) / RE));
+  router_logits_kernel<<<grid, 256, 0, s>>>(x, wr, T, H, E, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_select(const float* logits, const float* bias, int64_t T, int32_t E,
+                               int32_t G, int32_t Mg, int32_t K, int32_t* topk_idx,
+                               float* gates, int32_t* counts, hipStream_t s) {
+  fill_i32_kernel<<<(E + 255) / 256, 256, 0, s>>>(counts, E, 0);
+  if (T == 0) return hipGetLastError();
+  const dim3 grid(static_cast<unsigned>((T + 3) / 4));
+  const size_t lds = sizeof(float) * 4 * static_cast<size_t>(E);
+  const int slots = (E + 63) / 64;
+  if (slots <= 1)
+    route_select_kernel<1><<<grid, 256, lds, s>>>(logits, bias, T, E, G, Mg, K, topk_idx, gates, counts);
+  else if (slots <= 2)
+    route_select_kernel<2><<<grid, 256, lds, s>>>(logits, bias, T, E, G, Mg, K, topk_idx, gates, counts);
+  else if (slots <= 4)
+    route_select_kernel<4><<<grid, 256, lds, s>>>(logits, bias, T, E, G, Mg, K, topk_idx, gates, counts);
+  else if (slots <= 8)
+    route_select_kernel<8><<<grid, 256, lds, s>>>(logits, bias, T, E, G, Mg, K, topk_idx, gates, counts);
+  else
+    route_select_kernel<16><<<grid, 256, lds, s>>>(logits, bias, T, E, G, Mg, K, topk_idx, gates, counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const int32_t* topk_idx, const float* gates, int64_t T, int32_t E,
+                          int32_t K, const int32_t* counts, int32_t* offsets, int32_t* perm,
+                          int32_t* inv, float* row_gate, int32_t* offsets_ext, hipStream_t s) {
+  offsets_kernel<<<1, 1024, 0, s>>>(counts, E, offsets, offsets_ext, T);
+  if (T == 0) return hipGetLastError();
+  rank_kernel<<<E, 256, 0, s>>>(topk_idx, gates, T, E, K, offsets, perm, inv, row_gate,
+                                offsets_ext != nullptr ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_update_bias(float* bias, const int32_t* counts, int32_t E, int64_t T,
+                              int32_t K, float gamma, hipStream_t s) {
+  update_bias_kernel<<<(E + 255) / 256, 256, 0, s>>>(bias, counts, E, T, K, gamma);
+  return hipGetLastError();
+}
+
+}  // namespace dsmoe

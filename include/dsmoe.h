@@ -1,0 +1,283 @@
+/*
+ * dsmoe.h -- C ABI of a DeepSeekMoE FFN layer forward on the fine-grained
+ * FP8 recipe, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (cited by page and section):
+ *   "V3 notes"      xutianle.me, "DeepSeek-V3 技术报告：从 671B MoE 到低成本训练系统"
+ *   "infra answer"  51itzy.com DeepSeek-V3 Q&A page, the answer written from
+ *                   the infrastructure point of view (FP8 and routing paragraphs)
+ *   "evolution"     the "deepseek-evolution" blog post, V3 sections
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument except `stream` and the host-side descriptor
+ *   structs is a DEVICE pointer.  The caller owns all memory; the library
+ *   never allocates or frees, and keeps no mutable global state.
+ * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *   NULL is the default stream) and never synchronises the host.
+ * - Arguments are validated on the host before anything is enqueued.  On a
+ *   validation failure the call returns a non-zero status and launches
+ *   nothing.  A failed launch returns DSMOE_ERR_LAUNCH.  Faults inside a
+ *   kernel surface at the caller's next synchronisation.
+ * - Sizes of 0 rows / tokens are valid and enqueue nothing (status OK).
+ * - Alignment: FP8 code, bf16 and output matrices must be 16-byte aligned;
+ *   float and int32 arrays 4-byte aligned.  Row lengths that are multiples
+ *   of 128 keep every row 16-byte aligned.
+ * - Values: the library computes on finite inputs; NaN/Inf inputs give
+ *   unspecified (but memory-safe) results.  No flush of float32 subnormals.
+ * - FP8 is OCP E4M3FN (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ *   no infinities, max 448), the format the pages prescribe for every FP8
+ *   tensor (infra answer, FP8 paragraph; V3 notes §6).  Codes are stored as
+ *   uint8.
+ * - Calls on different streams with disjoint output buffers may overlap.
+ */
+#ifndef DSMOE_H
+#define DSMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsmoe_status {
+  DSMOE_OK = 0,
+  DSMOE_ERR_NULL = 1,      /* a required pointer is NULL */
+  DSMOE_ERR_SHAPE = 2,     /* a size is out of range or not a multiple of 128 */
+  DSMOE_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
+  DSMOE_ERR_DTYPE = 4,     /* unknown dtype code */
+  DSMOE_ERR_WORKSPACE = 5, /* workspace missing or smaller than required */
+  DSMOE_ERR_DEVICE = 6,    /* no usable device, or it is not gfx950 */
+  DSMOE_ERR_LAUNCH = 7     /* a kernel launch failed (hipGetLastError) */
+} dsmoe_status;
+
+typedef enum dsmoe_dtype {
+  DSMOE_BF16 = 0,          /* bfloat16, stored as uint16 */
+  DSMOE_F32 = 1            /* IEEE binary32 */
+} dsmoe_dtype;
+
+/* Static string naming a status code ("DSMOE_OK", ...); never NULL. */
+const char* dsmoe_status_str(int status);
+
+/* Version of this ABI (incremented on incompatible changes). */
+int dsmoe_abi_version(void);
+
+/* Limits checked by the calls below. */
+#define DSMOE_MAX_EXPERTS 1024
+#define DSMOE_MAX_GROUPS 64
+#define DSMOE_MAX_TOPK 32
+
+/*
+ * dsmoe_quant_act_1x128 -- fine-grained activation quantisation.
+ * Source: V3 notes §6.1 (activations scaled per 1x128 tile: one scale per
+ * token per 128 channels, computed online from the current tensor); infra
+ * answer, FP8 paragraph ("per-tile 1x128").
+ *
+ *   x      [rows][cols] row-major, dtype xt (DSMOE_BF16 or DSMOE_F32)
+ *   q      [rows][cols] uint8 E4M3FN codes (output)
+ *   scale  [rows][cols/128] float32 (output)
+ *
+ * For every row r and tile j: amax = max |x[r][128j .. 128j+127]| (exact),
+ * s = fl32(amax / 448) by IEEE float32 division (s = 1 when amax = 0),
+ * q = E4M3(fl32(x / s)) by IEEE float32 division, rounding to nearest with
+ * ties to even, saturating at +-448, keeping the sign of zero.
+ * Requires cols % 128 == 0, rows >= 0.
+ */
+dsmoe_status dsmoe_quant_act_1x128(const void* x, int xt, int64_t rows, int64_t cols,
+                                   uint8_t* q, float* scale, void* stream);
+
+/*
+ * dsmoe_quant_w_128x128 -- fine-grained weight quantisation.
+ * Source: V3 notes §6.1 (weights scaled per 128x128 block, online); infra
+ * answer, FP8 paragraph ("per-group 128x128").
+ *
+ *   w      [n_mats][N][K] row-major (N = output channels, K = input
+ *          channels), dtype wt (DSMOE_BF16 or DSMOE_F32)
+ *   q      [n_mats][N][K] uint8 E4M3FN codes (output)
+ *   scale  [n_mats][N/128][K/128] float32 (output)
+ *
+ * The same rule as dsmoe_quant_act_1x128 with amax taken over each 128x128
+ * block.  Requires N % 128 == 0, K % 128 == 0, n_mats >= 0.
+ */
+dsmoe_status dsmoe_quant_w_128x128(const void* w, int wt, int64_t n_mats, int64_t N, int64_t K,
+                                   uint8_t* q, float* scale, void* stream);
+
+/*
+ * dsmoe_route -- auxiliary-loss-free, group-limited top-K routing and the
+ * token permute.
+ * Source: V3 notes §4 (top-K chosen on s + b, gate weights from the raw
+ * affinity s), §4.2 (each token limited to experts on at most 4 nodes, no
+ * token dropping), §2 (8 of 256 routed experts per token); infra answer,
+ * routing paragraph (group routing to at most 4 nodes).
+ *
+ *   logits   [T][E] float32 router logits z
+ *   bias     [E] float32 per-expert bias b (read only)
+ *   topk_idx [T][K] int32 (output) chosen experts, in the order
+ *            (key descending, expert index ascending)
+ *   gates    [T][K] float32 (output) s_k / sum of s over the chosen experts,
+ *            summed in float32 in the order of topk_idx
+ *   counts   [E] int32 (output) tokens routed to each expert
+ *   offsets  [E+1] int32 (output) exclusive prefix sum of counts
+ *   perm     [T*K] int32 (output) row -> token; rows grouped by expert in
+ *            ascending expert order, tokens ascending within an expert
+ *   inv      [T][K] int32 (output) (token, k) -> row of perm
+ *
+ * s = fl32(sigmoid(z)) evaluated in float64; key = fl32(s + b); the E experts
+ * form G contiguous groups; a group's score is the float32 sum (largest first)
+ * of its ceil(K/Mg) largest keys; the Mg best groups are kept under (score
+ * descending, group index ascending); the K best experts of the kept groups
+ * are chosen under (key descending, index ascending).  Deterministic.
+ * Requires 1 <= E <= DSMOE_MAX_EXPERTS, 1 <= G <= DSMOE_MAX_GROUPS, E % G == 0,
+ * 1 <= Mg <= G, 1 <= K <= min(DSMOE_MAX_TOPK, Mg*E/G), T*K < 2^31.
+ */
+dsmoe_status dsmoe_route(const float* logits, const float* bias, int64_t T, int32_t E,
+                         int32_t G, int32_t Mg, int32_t K, int32_t* topk_idx, float* gates,
+                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                         void* stream);
+
+/*
+ * dsmoe_fp8_grouped_gemm -- block-scaled FP8 GEMM over groups of rows, with
+ * the partial sum of every 128-wide K chunk promoted to float32.
+ * Source: V3 notes §6.2 (partial sums promoted to FP32 every 128 FP8
+ * products), §6 (FP8 GEMM inputs, BF16/FP32 outputs), §6.1 (scale layouts);
+ * evolution, FP8 section.
+ *
+ *   a        [*][K] uint8 E4M3FN codes, a_scale [*][K/128] float32
+ *   a_rows   [M_total] int32 or NULL: output row r reads A row a_rows[r]
+ *            (NULL: A row r)
+ *   offsets  [G+1] int32 on the device: group g owns output rows
+ *            offsets[g] .. offsets[g+1]-1; offsets[0] = 0, non-decreasing,
+ *            offsets[G] <= M_total (rows past offsets[G] are left untouched)
+ *   w        [G][N][K] uint8 codes (W_g^T layout: output channel major),
+ *   w_scale  [G][N/128][K/128] float32
+ *   c        [M_total][N] (output), dtype ct (DSMOE_BF16 rounds to nearest
+ *            even, DSMOE_F32)
+ *
+ * c[r][n] = sum over chunks j of a_scale[ar][j] * w_scale[g][n/128][j] *
+ * (sum over k in chunk j of a[ar][k] * w[g][n][k]), ar = a_rows ? a_rows[r] : r.
+ * G = 1 with offsets = {0, M} is the dense GEMM.  The group sizes are read
+ * on the device; the host never synchronises.
+ * Requires N % 128 == 0, K % 128 == 0, 1 <= G, M_total >= 0.
+ */
+dsmoe_status dsmoe_fp8_grouped_gemm(const uint8_t* a, const float* a_scale,
+                                    const int32_t* a_rows, const int32_t* offsets, int32_t G,
+                                    int64_t M_total, const uint8_t* w, const float* w_scale,
+                                    int64_t N, int64_t K, void* c, int ct, void* stream);
+
+/*
+ * Layer description.  Source: V3 notes §2 (one shared expert, 256 routed
+ * experts of intermediate size 2048, 8 chosen) and §4.2 (at most 4 of 8
+ * nodes).  H hidden size, I expert intermediate size (both multiples of
+ * 128), E routed experts in G groups, Mg groups kept, K experts chosen,
+ * n_shared shared experts (0 or 1; intermediate size I, gate 1).
+ */
+typedef struct dsmoe_moe_desc {
+  int64_t H, I;
+  int32_t E, G, Mg, K, n_shared;
+} dsmoe_moe_desc;
+
+/*
+ * Layer weights (device pointers, read only), quantised with
+ * dsmoe_quant_w_128x128:
+ *   w13     [E][2I][H] codes, s13 [E][2I/128][H/128]: rows 0..I-1 of an
+ *           expert are the gate projection, rows I..2I-1 the up projection
+ *   w2      [E][H][I] codes,  s2  [E][H/128][I/128]: down projection
+ *   w13_sh, s13_sh, w2_sh, s2_sh: the shared expert, same layouts (one
+ *           matrix each); ignored when n_shared == 0
+ *   router_w [E][H] bf16: the router is kept in high precision, not FP8
+ *           (V3 notes §6: sensitive / cheap modules stay in higher precision)
+ */
+typedef struct dsmoe_moe_weights {
+  const uint8_t* w13;
+  const float* s13;
+  const uint8_t* w2;
+  const float* s2;
+  const uint8_t* w13_sh;
+  const float* s13_sh;
+  const uint8_t* w2_sh;
+  const float* s2_sh;
+  const void* router_w;
+} dsmoe_moe_weights;
+
+/*
+ * Optional device buffers that receive the layer's intermediates (each
+ * pointer may be NULL):  qx [T][H] and sx [T][H/128] (the 1x128 codes of x),
+ * logits [T][E], topk_idx and gates [T][K], offsets [E+1], perm [T*K],
+ * inv [T][K].
+ * stage_events (host array, may be NULL): DSMOE_STAGE_EVENTS hipEvent_t
+ * handles (passed as void*) created by the caller; event 0 is recorded on
+ * the stream before the first kernel and event i after stage i:
+ * 1 quantise x, 2 router logits, 3 top-K selection, 4 permute,
+ * 5 gate/up GEMM + SwiGLU + requant, 6 routed down GEMM,
+ * 7 shared down GEMM + combine.  Recording them changes no result.
+ */
+#define DSMOE_STAGE_EVENTS 8
+typedef struct dsmoe_moe_debug {
+  uint8_t* qx;
+  float* sx;
+  float* logits;
+  int32_t* topk_idx;
+  float* gates;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv;
+  void* const* stage_events;
+} dsmoe_moe_debug;
+
+/* Bytes of device workspace dsmoe_moe_forward needs for T tokens
+ * (0 if the description is invalid). */
+size_t dsmoe_moe_workspace_bytes(const dsmoe_moe_desc* d, int64_t T);
+
+/*
+ * dsmoe_moe_forward -- the DeepSeekMoE FFN layer forward on FP8.
+ * Source: V3 notes §2 (layer structure; the output is the shared expert's
+ * output plus the gate-weighted outputs of the chosen routed experts), §4
+ * and §4.2 (routing), §6 / §6.1 / §6.2 (FP8 recipe); infra answer (SwiGLU
+ * as the expert activation).
+ *
+ *   d, w       host pointers to the description and weight table
+ *   bias       [E] float32 routing bias (read only; see dsmoe_update_bias)
+ *   x          [T][H] bf16 layer input
+ *   y          [T][H] output, dtype yt (DSMOE_BF16 or DSMOE_F32)
+ *   counts_out [E] int32 per-expert token counts of this call (required:
+ *              it is what dsmoe_update_bias consumes)
+ *   workspace  device buffer of at least dsmoe_moe_workspace_bytes(d, T)
+ *              bytes, 256-byte aligned; contents on entry are ignored
+ *   dbg        host pointer to a dsmoe_moe_debug or NULL
+ *
+ * Steps: x is quantised per 1x128 tile; logits = x . router_w^T (bf16
+ * inputs, float32 accumulation); routing as dsmoe_route; every (token,
+ * expert) pair runs h = x W13^T (block-scaled FP8 GEMM, promoted per 128),
+ * a = silu(h_gate) * h_up in float32, a re-quantised per 1x128 tile,
+ * o = a W2^T (block-scaled FP8 GEMM) scaled by the gate; the shared expert
+ * runs the same FFN on every token with gate 1; y[t] = o_shared[t] + sum over
+ * k of o[t, k], summed in float32 in a fixed order, then rounded to yt.
+ * No residual add.  Deterministic: two calls with the same inputs give
+ * identical bits.
+ */
+dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights* w,
+                               const float* bias, const void* x, int64_t T, void* y, int yt,
+                               int32_t* counts_out, void* workspace, size_t ws_bytes,
+                               const dsmoe_moe_debug* dbg, void* stream);
+
+/*
+ * dsmoe_update_bias -- auxiliary-loss-free bias update.
+ * Source: V3 notes §4 (after each step an overloaded expert's bias is
+ * lowered and an underloaded expert's raised), §4.1 (speed gamma = 0.001);
+ * evolution, load-balancing section.
+ *
+ *   bias    [E] float32, updated in place:
+ *           b[e] = fl32(b[e] + fl32(gamma) * sign(T*K - E*counts[e])),
+ *           sign(0) = 0 (mean load T*K/E compared with counts exactly)
+ *   counts  [E] int32 loads of the step (e.g. counts_out of the forward)
+ * Requires 1 <= E <= DSMOE_MAX_EXPERTS, T >= 0, K >= 1.
+ */
+dsmoe_status dsmoe_update_bias(float* bias, const int32_t* counts, int32_t E, int64_t T,
+                               int32_t K, float gamma, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSMOE_H */

@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/dsmoe.h declares, and rejects invalid arguments with
+the documented status before touching any device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dsmoe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsmoe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    import fp8_block_scaled_dsmoe_amd as d
+    names = _declared()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(d.lib, n), f"{n} not exported"
+    assert sorted(d.EXPORTED) == names
+
+
+def test_status_strings_and_version():
+    import fp8_block_scaled_dsmoe_amd as d
+    assert d.lib.dsmoe_abi_version() == 1
+    want = ["DSMOE_OK", "DSMOE_ERR_NULL", "DSMOE_ERR_SHAPE", "DSMOE_ERR_ALIGN", "DSMOE_ERR_DTYPE",
+            "DSMOE_ERR_WORKSPACE", "DSMOE_ERR_DEVICE", "DSMOE_ERR_LAUNCH"]
+    for i, w in enumerate(want):
+        assert d.lib.dsmoe_status_str(i).decode() == w
+    assert d.lib.dsmoe_status_str(99).decode() == "DSMOE_ERR_UNKNOWN"
+
+
+def test_workspace_size_is_host_arithmetic():
+    import fp8_block_scaled_dsmoe_amd as d
+    desc = d.MoEDesc(7168, 2048, 256, 8, 4, 8, 1)
+    ws = d.moe_workspace_bytes(desc, 4096)
+    tk = 4096 * 8
+    # the two largest regions: routed outputs (f32) and the FP8 SwiGLU output
+    assert ws >= tk * 7168 * 4 + (tk + 4096) * 2048
+    assert ws < 2 * (tk * 7168 * 4 + (tk + 4096) * 2048)
+    assert d.moe_workspace_bytes(d.MoEDesc(7168, 2048, 256, 8, 4, 8, 1), 0) > 0
+    assert d.moe_workspace_bytes(d.MoEDesc(100, 2048, 256, 8, 4, 8, 1), 4096) == 0   # H % 128
+    assert d.moe_workspace_bytes(d.MoEDesc(7168, 2048, 256, 7, 4, 8, 1), 4096) == 0  # E % G
+    assert d.moe_workspace_bytes(d.MoEDesc(7168, 2048, 256, 8, 1, 64, 1), 4096) == 0  # K > 32
+
+
+def _vp(v):
+    return ctypes.c_void_p(v)
+
+
+ALIGNED = 1 << 20          # fake, never dereferenced: validation fails before any use
+MISALIGNED = ALIGNED + 2
+
+
+def test_quant_validation_errors():
+    import fp8_block_scaled_dsmoe_amd as d
+    L = d.lib
+    assert L.dsmoe_quant_act_1x128(_vp(ALIGNED), 7, 4, 128, _vp(ALIGNED), _vp(ALIGNED), None) == 4
+    assert L.dsmoe_quant_act_1x128(_vp(ALIGNED), 0, 4, 100, _vp(ALIGNED), _vp(ALIGNED), None) == 2
+    assert L.dsmoe_quant_act_1x128(_vp(ALIGNED), 0, -1, 128, _vp(ALIGNED), _vp(ALIGNED), None) == 2
+    assert L.dsmoe_quant_act_1x128(None, 0, 4, 128, _vp(ALIGNED), _vp(ALIGNED), None) == 1
+    assert L.dsmoe_quant_act_1x128(_vp(MISALIGNED), 0, 4, 128, _vp(ALIGNED), _vp(ALIGNED), None) == 3
+    assert L.dsmoe_quant_act_1x128(None, 0, 0, 128, None, None, None) == 0       # empty: no-op
+    assert L.dsmoe_quant_w_128x128(_vp(ALIGNED), 0, 1, 130, 128, _vp(ALIGNED), _vp(ALIGNED), None) == 2
+    assert L.dsmoe_quant_w_128x128(_vp(ALIGNED), 0, 1, 128, 128, None, _vp(ALIGNED), None) == 1
+    assert L.dsmoe_quant_w_128x128(_vp(ALIGNED), 0, 1, 128, 128, _vp(ALIGNED), _vp(MISALIGNED), None) == 3
+
+
+def test_route_and_bias_validation_errors():
+    import fp8_block_scaled_dsmoe_amd as d
+    L = d.lib
+    p = [_vp(ALIGNED)] * 8
+    assert L.dsmoe_route(p[0], p[1], 10, 16, 3, 2, 2, *p[2:], None) == 2        # E % G
+    assert L.dsmoe_route(p[0], p[1], 10, 16, 4, 5, 2, *p[2:], None) == 2        # Mg > G
+    assert L.dsmoe_route(p[0], p[1], 10, 16, 4, 2, 9, *p[2:], None) == 2        # K > Mg*E/G
+    assert L.dsmoe_route(p[0], p[1], 10, 2048, 8, 4, 8, *p[2:], None) == 2      # E too large
+    assert L.dsmoe_route(p[0], p[1], 10, 256, 8, 4, 33, *p[2:], None) == 2      # K too large
+    assert L.dsmoe_route(None, p[1], 10, 16, 4, 2, 2, *p[2:], None) == 1
+    assert L.dsmoe_route(p[0], p[1], 10, 16, 4, 2, 2, _vp(MISALIGNED), *p[3:], None) == 3
+    assert L.dsmoe_update_bias(_vp(ALIGNED), _vp(ALIGNED), 0, 10, 2, 0.001, None) == 2
+    assert L.dsmoe_update_bias(None, _vp(ALIGNED), 16, 10, 2, 0.001, None) == 1
+    assert L.dsmoe_update_bias(_vp(ALIGNED), _vp(ALIGNED), 16, 10, 0, 0.001, None) == 2
+
+
+def test_gemm_validation_errors():
+    import fp8_block_scaled_dsmoe_amd as d
+    L = d.lib
+    a = _vp(ALIGNED)
+    assert L.dsmoe_fp8_grouped_gemm(a, a, None, a, 1, 64, a, a, 100, 128, a, 0, None) == 2
+    assert L.dsmoe_fp8_grouped_gemm(a, a, None, a, 0, 64, a, a, 128, 128, a, 0, None) == 2
+    assert L.dsmoe_fp8_grouped_gemm(a, a, None, a, 1, 64, a, a, 128, 128, a, 5, None) == 4
+    assert L.dsmoe_fp8_grouped_gemm(a, a, None, None, 1, 64, a, a, 128, 128, a, 0, None) == 1
+    assert L.dsmoe_fp8_grouped_gemm(a, a, None, a, 1, 64, _vp(MISALIGNED), a, 128, 128, a, 0, None) == 3
+    assert L.dsmoe_fp8_grouped_gemm(None, None, None, None, 1, 0, None, None, 128, 128, None, 0, None) == 0
+
+
+def test_moe_forward_validation_errors():
+    import fp8_block_scaled_dsmoe_amd as d
+    L = d.lib
+    desc = d._Desc(7168, 2048, 256, 8, 4, 8, 1)
+    w = d._Weights(*([ALIGNED] * 9))
+    a = _vp(ALIGNED)
+    need = L.dsmoe_moe_workspace_bytes(ctypes.byref(desc), 64)
+    args = lambda **kw: dict(dict(d=ctypes.byref(desc), w=ctypes.byref(w), bias=a, x=a, T=64, y=a, yt=0,
+                                  counts=a, ws=a, ws_bytes=need, dbg=None, stream=None), **kw)
+    call = lambda kw: L.dsmoe_moe_forward(*args(**kw).values())
+    assert call({"ws_bytes": need - 1}) == 5
+    assert call({"ws": None}) == 5
+    assert call({"yt": 3}) == 4
+    assert call({"counts": None}) == 1
+    assert call({"x": _vp(MISALIGNED)}) == 3
+    bad = d._Desc(7168, 2048, 256, 8, 4, 8, 2)
+    assert call({"d": ctypes.byref(bad)}) == 2
+    w_null = d._Weights(*([ALIGNED] * 4 + [None] + [ALIGNED] * 4))
+    assert call({"w": ctypes.byref(w_null)}) == 1

@@ -1,0 +1,113 @@
+"""GPU parity of dsmoe_quant_act_1x128 / dsmoe_quant_w_128x128 against the
+oracle: FP8 codes and scales must match bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+from dsmoe_inputs import bf16_round, dense_gemm_inputs_host, normal_bf16
+from gpu_util import banner, dev, host
+from oracle import quant as oq
+
+pytestmark = pytest.mark.gpu
+
+
+def _dsmoe():
+    import fp8_block_scaled_dsmoe_amd as d
+    return d
+
+
+def _check_act(x32: np.ndarray, as_bf16: bool, what: str):
+    d = _dsmoe()
+    banner(f"quant_act {what} shape={x32.shape} bf16={as_bf16}")
+    xt = dev(x32, torch.bfloat16 if as_bf16 else torch.float32)
+    q, s = d.quant_act_1x128(xt)
+    qo, so = oq.quant_act_1x128(x32)
+    qg, sg = host(q), host(s)
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32)), f"{what}: scales differ"
+    bad = np.argwhere(qg != qo)
+    assert bad.size == 0, f"{what}: {len(bad)} codes differ, first {bad[:5].tolist()}"
+
+
+def test_golden_tiles(golden):
+    g = golden("quant_tiles.json")
+    row = np.zeros((1, 256), np.float32)
+    for k, v in g["tile0_nonzero"].items():
+        row[0, int(k)] = float(v)
+    for k, v in g["tile1_nonzero"].items():
+        row[0, 128 + int(k)] = float(v)
+    _check_act(row, True, "golden bf16")
+    _check_act(row, False, "golden f32")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 128), (300, 1024), (4096, 7168)])
+def test_act_bf16_with_outliers(rows, cols):
+    a, _ = dense_gemm_inputs_host(rows, 128, cols, seed=rows)
+    _check_act(a, True, f"outliers {rows}x{cols}")
+
+
+def test_act_f32_encoder_sweep():
+    # tiles whose first element is 448 have scale exactly 1, so every other
+    # element is encoded as given: sweep sign, every exponent that reaches the
+    # E4M3 range (including float32 subnormals), every top-7 mantissa pattern,
+    # and low bits at / just around the rounding midpoints
+    r = np.random.default_rng(0)
+    exps = np.arange(0, 136, dtype=np.uint32)            # biased float32 exponents 0..135 (< 512)
+    mant_hi = np.arange(128, dtype=np.uint32) << 16
+    lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    bits = (exps[:, None, None] << 23) | mant_hi[None, :, None] | lows[None, None, :]
+    bits = bits.reshape(-1)
+    bits = np.concatenate([bits, bits | 0x80000000,
+                           r.integers(0, 0x43E00000, size=200000, dtype=np.uint32)])
+    vals = bits.view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 448.0)]
+    per = 127
+    n_tiles = -(-vals.size // per)
+    pad = np.zeros(n_tiles * per, np.float32)
+    pad[:vals.size] = vals
+    tiles = np.concatenate([np.full((n_tiles, 1), 448.0, np.float32), pad.reshape(n_tiles, per)], axis=1)
+    cols = 1024
+    n_rows = -(-tiles.size // cols)
+    flat = np.zeros(n_rows * cols, np.float32)
+    flat[:tiles.size] = tiles.reshape(-1)
+    x = flat.reshape(n_rows, cols)
+    # every tile of x starts with 448 (tile boundaries are 128-aligned)
+    assert np.all(x.reshape(-1, 128)[: tiles.shape[0], 0] == 448.0)
+    _check_act(x, False, "encoder sweep")
+
+
+def test_act_zero_and_negative_zero_tiles():
+    x = np.zeros((3, 256), np.float32)
+    x[1, :128] = -0.0
+    x[2, 128:] = bf16_round(np.linspace(-1e-38, 1e-38, 128).astype(np.float32))
+    _check_act(x, False, "zero tiles")
+    _check_act(x, True, "zero tiles")
+
+
+def test_act_empty():
+    d = _dsmoe()
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    q, s = d.quant_act_1x128(x)
+    assert q.shape == (0, 256) and s.shape == (0, 2)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_weights_small(dtype):
+    d = _dsmoe()
+    w = normal_bf16("qw_small", (3, 384, 640), 0.02, seed=1)
+    w[1, 5, 7] = 3.0    # an outlier in one block
+    banner(f"quant_w small {dtype}")
+    q, s = d.quant_w_128x128(dev(w, dtype))
+    qo, so = oq.quant_w_128x128(w)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), qo)
+
+
+def test_weights_v3_expert_shape():
+    d = _dsmoe()
+    w13 = normal_bf16("qw_v3_w13", (1, 4096, 7168), 0.02, seed=2)
+    banner("quant_w v3 expert w13")
+    q, s = d.quant_w_128x128(dev(w13, torch.bfloat16))
+    qo, so = oq.quant_w_128x128(w13)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), qo)

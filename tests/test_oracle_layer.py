@@ -134,3 +134,27 @@ def test_zero_input_gives_zero_output():
     out = layer.moe_layer(x, d["router_w"], d["bias"], get, get(cfg.E), cfg.G, cfg.Mg, cfg.K)
     assert np.all(out["y"] == 0)
     assert out["counts"].sum() == cfg.T * cfg.K
+
+
+def test_requant_slack_flags_codes_at_midpoints_only():
+    # one 128-wide tile with amax 448 (scale 1): 17 sits on the 16/18 midpoint,
+    # 16 is a code value, 17.5 is a quarter step from every midpoint
+    a = np.zeros((1, 128), np.float32)
+    a[0, :4] = [448.0, 17.0, 16.0, 17.5]
+    qa, sa = quant.quant_act_1x128(a)
+    assert sa[0, 0] == 1.0
+    h = np.zeros((1, 256))
+    h_d = np.zeros((1, 256))
+    w2 = np.zeros((128, 128), np.float32)
+    w2[:, 1] = 0.5
+    w2[:, 2] = 0.25
+    w2[:, 3] = 0.125
+    w2[0, 0] = 448.0 * 2.0 ** -10          # sets every block scale to 2^-10
+    q2, s2 = quant.quant_w_128x128(w2)
+    slack, n_amb = layer.requant_slack(h, h_d, a, qa, sa, q2, s2, 0.0)
+    assert n_amb == 1
+    # only column 1 counts: step of code 16 is max(16-15, 18-16) = 2
+    assert np.allclose(slack[0], 2 * np.abs(w2[:, 1]))
+    # a large error bound makes every non-zero element ambiguous
+    _, n_all = layer.requant_slack(h + 1.0, np.ones((1, 256)) * 1e3, a, qa, sa, q2, s2, 1.0)
+    assert n_all == 128
