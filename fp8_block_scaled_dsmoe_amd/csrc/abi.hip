@@ -12,6 +12,7 @@
 namespace {
 
 constexpr int64_t kI32Max = 2147483647LL;
+constexpr int64_t kMaxK = 32768;   // contraction length limit of the FP8 GEMM (256 chunks)
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -85,6 +86,7 @@ Layout layout_for(const dsmoe_moe_desc& d, int64_t T) {
 dsmoe_status check_desc(const dsmoe_moe_desc* d, int64_t T) {
   if (!d) return DSMOE_ERR_NULL;
   if (d->H <= 0 || d->I <= 0 || d->H % 128 || d->I % 128) return DSMOE_ERR_SHAPE;
+  if (d->H > kMaxK || d->I > kMaxK) return DSMOE_ERR_SHAPE;
   if (d->n_shared != 0 && d->n_shared != 1) return DSMOE_ERR_SHAPE;
   const dsmoe_status s = check_routing_shape(T, d->E, d->G, d->Mg, d->K);
   if (s != DSMOE_OK) return s;
@@ -165,8 +167,9 @@ dsmoe_status dsmoe_fp8_grouped_gemm(const uint8_t* a, const float* a_scale,
                                     int64_t N, int64_t K, void* c, int ct, void* stream) {
   if (!valid_dtype(ct)) return DSMOE_ERR_DTYPE;
   if (G < 1 || M_total < 0 || N <= 0 || K <= 0 || N % 128 || K % 128) return DSMOE_ERR_SHAPE;
+  if (K > kMaxK) return DSMOE_ERR_SHAPE;
   if (M_total > kI32Max || G > kI32Max / 2) return DSMOE_ERR_SHAPE;
-  if (((M_total + 127) / 128 + G) * (N / 128) >= kI32Max) return DSMOE_ERR_SHAPE;
+  if (((M_total + 15) / 16 + G) * (N / 128) >= kI32Max) return DSMOE_ERR_SHAPE;  // grid of the smallest tiles
   if (M_total == 0) return DSMOE_OK;
   if (!a || !a_scale || !offsets || !w || !w_scale || !c) return DSMOE_ERR_NULL;
   if (!aligned(a, 16) || !aligned(w, 16) || !aligned(c, 16) || !aligned(a_scale, 4) ||
@@ -189,6 +192,7 @@ dsmoe_status dsmoe_fp8_grouped_gemm(const uint8_t* a, const float* a_scale,
   p.c_f32 = ct == DSMOE_F32;
   p.epi = dsmoe::Epilogue::kStore;
   p.row_limit = M_total;
+  p.rows_hint = (M_total + G - 1) / G;
   return launch_status(dsmoe::launch_grouped_gemm(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -300,6 +304,7 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
   g1.c_scale = sa;
   g1.epi = dsmoe::Epilogue::kSwiGLUQuant;
   g1.row_limit = g1.M_total;
+  g1.rows_hint = (T * K + E - 1) / E;
   DSMOE_TRY(dsmoe::launch_grouped_gemm(g1, st));
   DSMOE_MARK(5);
 
@@ -320,6 +325,7 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
   g2.row_gate = row_gate;
   g2.epi = dsmoe::Epilogue::kGateStore;
   g2.row_limit = g2.M_total;
+  g2.rows_hint = (T * K + E - 1) / E;
   DSMOE_TRY(dsmoe::launch_grouped_gemm(g2, st));
   DSMOE_MARK(6);
 
@@ -344,6 +350,7 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
     g3.row_base = T * K;
     g3.epi = dsmoe::Epilogue::kCombine;
     g3.row_limit = T * K + T;
+    g3.rows_hint = T;
     DSMOE_TRY(dsmoe::launch_grouped_gemm(g3, st));
   } else {
     DSMOE_TRY(dsmoe::launch_combine(o, inv, T, K, H, y, f32out, st));

@@ -11,10 +11,20 @@
 // accumulator and its result is the chunk's partial sum; the FP32
 // rescale-and-accumulate acc += P * (sa[row] * sw[block]) runs on the VALU.
 //
-// Tiling: block tile 128 rows x BN columns, K step 128 (one chunk), waves of
-// 64 x 64 (4 x 4 MFMA tiles).  A and W chunks are staged through LDS (double
-// buffered, 16-byte segments XOR-swizzled by row so MFMA operand reads are
-// bank-conflict free) with the next chunk prefetched into registers.
+// Two kernel shapes share the tile scheduling and the epilogues:
+//
+//  * gemm_lds_kernel -- groups of many rows (MFMA-bound).  Block tile 128
+//    rows x BN columns, waves of 64 x 64; A and W chunks are copied straight
+//    into a ring of LDS stages with gfx950's LDS DMA (global_load_lds), two
+//    chunks in flight while one is multiplied.
+//  * gemm_ws_kernel -- groups of few rows (HBM-bound on the weights, as in
+//    prefill at T=4096 and decode).  Block tile BM rows x 256 columns, eight
+//    waves of BM x 32; every wave streams its own W columns from HBM directly
+//    into MFMA operand registers, several chunks ahead, so the bytes in
+//    flight are not limited by LDS; only the small A tile goes through LDS.
+//    BM is chosen so that one tile holds a whole group, which makes every
+//    weight byte travel from HBM once.
+//
 // Rows of a group are gathered through a_rows (the token permute), so the
 // permuted activation matrix is never materialised.  Group sizes stay on the
 // device: every block derives its (group, row tile) from offsets[].  Logical
@@ -30,9 +40,9 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128;
 constexpr int BK = 128;
 constexpr int kXcds = 8;
+constexpr int kMaxChunks = 256;   // K <= 32768
 
 __device__ __forceinline__ int swz(int row, int seg) { return row * BK + ((seg ^ (row & 7)) << 4); }
 
@@ -43,11 +53,19 @@ __device__ __forceinline__ f32x4 mfma_chunk(const i32x8& a, const i32x8& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
-// Find the group and row range of global row-tile `mt` (tiles are numbered
-// group by group, ceil(n_g / BM) per group).  Returns false past the end.
-template <int THREADS>
-__device__ bool decode_tile(const int32_t* __restrict__ offsets, int32_t G, int64_t mt,
-                            int32_t* s_scan, int64_t* s_out) {
+__device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// Map a logical tile index to (group, column tile, row range).  Tiles are
+// numbered group by group; inside a group, column tile by column tile, and
+// inside a column tile, row tile by row tile.  The row tiles that share one
+// weight tile are therefore adjacent, run on the same XCD at the same time and
+// read that weight tile from HBM once (the second one hits L2).  s_out gets
+// {group, row0, row1, column tile}; returns false past the end.
+template <int THREADS, int TILE_M>
+__device__ bool decode_tile(const int32_t* __restrict__ offsets, int32_t G, int64_t logical,
+                            int64_t n_tiles, int64_t* s_scan, int64_t* s_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int NW = THREADS / 64;
   if (tid == 0) s_out[0] = -1;
@@ -58,31 +76,35 @@ __device__ bool decode_tile(const int32_t* __restrict__ offsets, int32_t G, int6
     if (g < G) {
       lo = offsets[g];
       hi = offsets[g + 1];
-      cnt = hi > lo ? (hi - lo + BM - 1) / BM : 0;
+      cnt = hi > lo ? (hi - lo + TILE_M - 1) / TILE_M : 0;
     }
-    // inclusive scan of cnt over the block
-    int32_t v = cnt;
+    // inclusive scan of the group's tile count (row tiles x column tiles)
+    const int64_t mine = static_cast<int64_t>(cnt) * n_tiles;
+    int64_t v = mine;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int32_t u = __shfl_up(v, o, 64);
+      const int64_t u = __shfl_up(v, o, 64);
       if (lane >= o) v += u;
     }
     if (lane == 63) s_scan[wave] = v;
     __syncthreads();
-    int32_t wbase = 0, total = 0;
+    int64_t wbase = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const int32_t t = s_scan[w];
+      const int64_t t = s_scan[w];
       if (w < wave) wbase += t;
       total += t;
     }
     const int64_t incl = carry + wbase + v;
-    const int64_t excl = incl - cnt;
-    if (cnt > 0 && mt >= excl && mt < incl) {
-      const int64_t r0 = lo + (mt - excl) * BM;
+    const int64_t excl = incl - mine;
+    if (mine > 0 && logical >= excl && logical < incl) {
+      const int64_t local = logical - excl;
+      const int64_t nt = local / cnt;
+      const int64_t r0 = lo + (local - nt * cnt) * TILE_M;
       s_out[0] = g;
       s_out[1] = r0;
-      s_out[2] = min<int64_t>(r0 + BM, hi);
+      s_out[2] = min<int64_t>(r0 + TILE_M, hi);
+      s_out[3] = nt;
     }
     carry += total;
     __syncthreads();
@@ -90,39 +112,273 @@ __device__ bool decode_tile(const int32_t* __restrict__ offsets, int32_t G, int6
   return s_out[0] >= 0;
 }
 
-template <int BN, Epilogue EPI>
-struct Kcfg {
-  static constexpr int WN = BN / 64;          // waves along N
-  static constexpr int THREADS = 2 * WN * 64; // 2 waves along M
-  static constexpr int A_LOADS = (BM * 8) / THREADS;   // 16-byte segments per thread
-  static constexpr int B_LOADS = (BN * 8) / THREADS;
+// Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8).  Logical tiles are handed out in rounds of 8 x kXcdRun: in every
+// round each XCD gets a run of kXcdRun consecutive tiles.  Consecutive tiles
+// (row tiles sharing a weight tile, column tiles sharing an A tile) thus share
+// an XCD's L2, while the useful tiles -- a prefix of the logical range, since
+// the grid is sized for the worst case -- are spread over all XCDs.  The grid
+// is padded to whole rounds so that the mapping is a bijection.
+constexpr int kXcdRun = 32;
+
+__device__ __forceinline__ int64_t xcd_logical_block() {
+  const int64_t bid = blockIdx.x;
+  const int64_t slot = bid / kXcds;
+  return (slot / kXcdRun) * (kXcds * kXcdRun) + (bid % kXcds) * kXcdRun + slot % kXcdRun;
+}
+
+inline int64_t pad_grid(int64_t blocks) {
+  const int64_t round = kXcds * kXcdRun;
+  return (blocks + round - 1) / round * round;
+}
+
+// ---------------------------------------------------------------------------
+// Shared epilogues.  A wave holds NI x NJ accumulator tiles of 16 x 16; lane
+// (i, j, r) holds local row row_base + 16i + 4*(lane/16) + r and column
+// col0 + 16j + lane%16 of the output; row0 is the tile's first output row.
+// ---------------------------------------------------------------------------
+template <int NI, int NJ, Epilogue EPI>
+__device__ __forceinline__ void epi_store(const GemmProblem& p, const f32x4 (&acc)[NI][NJ],
+                                          int64_t row0, int64_t row1, int row_base,
+                                          int64_t col0) {
+  const int lane = threadIdx.x & 63;
+  const int64_t N = p.N;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = row0 + row_base + i * 16 + (lane >> 4) * 4 + r;
+      if (row >= row1) continue;
+      float gsc = 1.0f;
+      if constexpr (EPI == Epilogue::kGateStore) gsc = p.row_gate[row];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t col = col0 + j * 16 + (lane & 15);
+        float v = acc[i][j][r];
+        if constexpr (EPI == Epilogue::kGateStore) v = v * gsc;
+        if (p.c_f32)
+          static_cast<float*>(p.c)[row * N + col] = v;
+        else
+          static_cast<uint16_t*>(p.c)[row * N + col] = f32_to_bf16(v);
+      }
+    }
+}
+
+// y[t][col] = acc + sum over k (ascending) of o[inv[t][k]][col].  Each
+// 16-row slice of the wave tile goes through the wave's own LDS scratch so
+// that a lane then owns a run of 4*NJ contiguous columns of one row and reads
+// the routed rows with 16/32-byte loads.
+template <int NI, int NJ>
+__device__ __forceinline__ void epi_combine(const GemmProblem& p, const f32x4 (&acc)[NI][NJ],
+                                            int64_t row0, int64_t row1, int row_base,
+                                            int64_t col0, float* scratch) {
+  constexpr int NCOL = 16 * NJ;
+  constexpr int PER = NCOL / 4;  // columns per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t N = p.N;
+  const int32_t K_ = p.topk;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        scratch[((lane >> 4) * 4 + r) * NCOL + j * 16 + (lane & 15)] = acc[i][j][r];
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    const int lr = lane >> 2;
+    const int lc = (lane & 3) * PER;
+    const int64_t row = row0 + row_base + i * 16 + lr;
+    float v[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) v[e] = scratch[lr * NCOL + lc + e];
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+    if (row < row1) {
+      const int64_t tok = row - p.row_base;
+      const int32_t* inv_t = p.inv + tok * K_;
+      const int64_t col = col0 + lc;
+      for (int k = 0; k < K_; ++k) {
+        const int64_t orow = inv_t[k];
+        if (p.c_f32) {
+          const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.o_routed) + orow * N + col);
+#pragma unroll
+          for (int q = 0; q < PER / 4; ++q) {
+            const f32x4 o4 = src[q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * q + e] = v[4 * q + e] + o4[e];
+          }
+        } else {
+          const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.o_routed) + orow * N + col);
+#pragma unroll
+          for (int q = 0; q < PER / 8; ++q) {
+            const u32x4 o8 = src[q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[8 * q + 2 * e] = v[8 * q + 2 * e] + __uint_as_float(o8[e] << 16);
+              v[8 * q + 2 * e + 1] = v[8 * q + 2 * e + 1] + __uint_as_float(o8[e] & 0xFFFF0000u);
+            }
+          }
+        }
+      }
+      if (p.c_f32) {
+        f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(p.c) + tok * N + col);
+#pragma unroll
+        for (int q = 0; q < PER / 4; ++q) dst[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+      } else {
+        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.c) + tok * N + col);
+#pragma unroll
+        for (int q = 0; q < PER / 8; ++q) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = static_cast<uint32_t>(f32_to_bf16(v[8 * q + 2 * e])) |
+                   (static_cast<uint32_t>(f32_to_bf16(v[8 * q + 2 * e + 1])) << 16);
+          dst[q] = w;
+        }
+      }
+    }
+  }
+}
+
+// SwiGLU + 1x128 requantisation.  The block tile holds 128 gate columns and
+// the matching 128 up columns; a gate wave owns gate columns
+// [gcol, gcol + 16*NJ) and one up wave owns the same up columns.  Up waves
+// hand their accumulators over through LDS; gate waves form
+// a = silu(g) * u in float32, the row amax over the 128 columns (across the
+// gate waves), the scale and the E4M3 codes; the codes are then stored with
+// 16-byte writes.  s_up: [ROWS][128] f32, s_rmax: [GATE_WAVES][ROWS] f32,
+// s_code: [ROWS][128] bytes.
+template <int NI, int NJ, int ROWS, int GATE_WAVES>
+__device__ __forceinline__ void epi_swiglu(const GemmProblem& p, const f32x4 (&acc)[NI][NJ],
+                                           int64_t row0, int64_t row1, int row_base,
+                                           bool is_gate, int gate_idx, int gcol, int64_t nt,
+                                           float* s_up, float* s_rmax, uint8_t* s_code) {
+  const int lane = threadIdx.x & 63;
+  const int frow = lane & 15;
+  if (!is_gate) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s_up[(row_base + i * 16 + (lane >> 4) * 4 + r) * 128 + gcol + j * 16 + frow] = acc[i][j][r];
+  }
+  __syncthreads();
+  float av[NI][NJ][4];
+  if (is_gate) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lr = row_base + i * 16 + (lane >> 4) * 4 + r;
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const float gt = acc[i][j][r];
+          const float up = s_up[lr * 128 + gcol + j * 16 + frow];
+          const float a = gt / (1.0f + expf(-gt)) * up;
+          av[i][j][r] = a;
+          m = fmaxf(m, fabsf(a));
+        }
+        m = wave_max_width(m, 16);
+        if (frow == 0) s_rmax[gate_idx * ROWS + lr] = m;
+      }
+  }
+  __syncthreads();
+  const int64_t I = p.N / 2;
+  if (is_gate) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lr = row_base + i * 16 + (lane >> 4) * 4 + r;
+        float amax = s_rmax[lr];
+#pragma unroll
+        for (int w = 1; w < GATE_WAVES; ++w) amax = fmaxf(amax, s_rmax[w * ROWS + lr]);
+        const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          s_code[lr * 128 + gcol + j * 16 + frow] = static_cast<uint8_t>(e4m3_encode(av[i][j][r] / s));
+        const int64_t row = row0 + lr;
+        if (gate_idx == 0 && frow == 0 && row < row1) p.c_scale[row * (I / BK) + nt] = s;
+      }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < ROWS * 8; idx += blockDim.x) {
+    const int lr = idx >> 3, seg = idx & 7;
+    const int64_t row = row0 + lr;
+    if (row < row1)
+      *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.c) + row * I + nt * 128 + seg * 16) =
+          *reinterpret_cast<const u32x4*>(&s_code[lr * 128 + seg * 16]);
+  }
+}
+
+// ===========================================================================
+// gemm_lds_kernel: 128-row tiles, LDS-DMA ring (groups of many rows)
+// ===========================================================================
+constexpr int LBM = 128;
+
+template <int BN>
+struct LdsCfg {
+  static constexpr int WN = BN / 64;            // waves along N
+  static constexpr int NW = 2 * WN;             // 2 waves along M
+  static constexpr int THREADS = NW * 64;
+  static constexpr int STAGES = BN == 256 ? 3 : 4;                 // LDS ring depth
+  static constexpr int A_WLOADS = LBM * BK / 1024;                 // 1 KB wave-loads per chunk
+  static constexpr int B_WLOADS = BN * BK / 1024;
+  static constexpr int PER_WAVE = (A_WLOADS + B_WLOADS) / NW;      // tile wave-loads per wave
+  static constexpr int LPS = PER_WAVE + 1;                         // + one for the row scales
+  static constexpr int ROWS_PER_WAVE = LBM / NW;                   // scale rows per wave
+  static_assert((A_WLOADS + B_WLOADS) % NW == 0, "uneven load split");
+  static_assert(LPS * (STAGES - 2) < 64, "vmcnt range");
 };
 
+// Asynchronous global -> LDS copies (gfx950 LDS DMA).  Each lane moves its
+// bytes to lds_base + lane * size; lds_base is wave-uniform (M0).  The data
+// lands asynchronously and is counted by vmcnt like any vector load; these
+// copies are issued from inline assembly so that the compiler neither waits
+// for them conservatively nor counts them, and the kernel waits for them
+// explicitly (vector memory operations of a wave complete in order).
+__device__ __forceinline__ void dma_16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_4(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
 template <int BN, Epilogue EPI>
-__global__ __launch_bounds__(2 * BN) void gemm_kernel(GemmProblem p, int64_t n_tiles) {
-  using C = Kcfg<BN, EPI>;
+__global__ __launch_bounds__(2 * BN) void gemm_lds_kernel(GemmProblem p, int64_t n_tiles) {
+  using C = LdsCfg<BN>;
   constexpr int THREADS = C::THREADS;
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][BN * BK];
-  __shared__ __attribute__((aligned(16))) float s_sa[2][BM];
-  __shared__ int32_t s_scan[THREADS / 64];
-  __shared__ int64_t s_tile[3];
+  constexpr int S = C::STAGES;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a[S][LBM * BK];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_b[S][BN * BK];
+  __shared__ __attribute__((aligned(256))) float s_sa[S][LBM];
+  __shared__ float s_sw[2][kMaxChunks];   // weight-block scales of the two 128-column halves
+  __shared__ int64_t s_scan[THREADS / 64];
+  __shared__ int64_t s_tile[4];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int wm = wave / C::WN, wn = wave % C::WN;
 
-  // XCD-aware logical tile id: blocks bid, bid+8, ... share an XCD; give
-  // each XCD a contiguous range of logical tiles.
-  const int64_t nblk = gridDim.x;
-  const int64_t bid = blockIdx.x;
-  const int64_t per_xcd = nblk / kXcds;
-  const int64_t logical = (bid % kXcds) * per_xcd + bid / kXcds;
-  const int64_t mt = logical / n_tiles;
-  const int64_t nt = logical - mt * n_tiles;
-
-  if (!decode_tile<THREADS>(p.offsets, p.G, mt, s_scan, s_tile)) return;
+  const int64_t logical = xcd_logical_block();
+  if (!decode_tile<THREADS, LBM>(p.offsets, p.G, logical, n_tiles, s_scan, s_tile)) return;
   const int32_t g = static_cast<int32_t>(s_tile[0]);
+  const int64_t nt = s_tile[3];
   const int64_t row0 = s_tile[1];
   const int64_t row1 = min(s_tile[2], p.row_limit);  // guards against offsets past the buffers
   if (row0 >= row1) return;
@@ -138,56 +394,60 @@ __global__ __launch_bounds__(2 * BN) void gemm_kernel(GemmProblem p, int64_t n_t
   const int64_t w_up_shift = (EPI == Epilogue::kSwiGLUQuant) ? N / 2 - 128 : 0;
 #define DSMOE_WROW(lc) (w_row_base + (lc) + ((lc) >= 128 ? w_up_shift : 0))
 
-  // per-thread global sources
-  const uint8_t* a_src[C::A_LOADS];
-  int a_lds[C::A_LOADS];
+  // This wave's share of every chunk: PER_WAVE wave-loads of 1 KB (8 tile
+  // rows each, lane -> row 8j + lane/8, physical segment lane%8 holding the
+  // logical K segment (lane%8) ^ (row%8), which realises the XOR swizzle)
+  // plus the 1x128 scales of ROWS_PER_WAVE tile rows.
+  const uint8_t* src[C::PER_WAVE];
+  uint32_t dst_off[C::PER_WAVE];
+  bool dst_is_a[C::PER_WAVE];
 #pragma unroll
-  for (int i = 0; i < C::A_LOADS; ++i) {
-    const int idx = tid + THREADS * i;
-    const int lr = idx >> 3, seg = idx & 7;
-    const int64_t r = row0 + lr < row1 ? row0 + lr : row0;
-    const int64_t src = p.a_rows ? p.a_rows[r] : r;
-    a_src[i] = p.a + src * K + seg * 16;
-    a_lds[i] = swz(lr, seg);
+  for (int i = 0; i < C::PER_WAVE; ++i) {
+    const int j = wave * C::PER_WAVE + i;
+    const bool is_a = j < C::A_WLOADS;
+    const int jj = is_a ? j : j - C::A_WLOADS;
+    const int row = jj * 8 + (lane >> 3);
+    const int lseg = (lane & 7) ^ (row & 7);
+    if (is_a) {
+      const int64_t r = row0 + row < row1 ? row0 + row : row0;
+      const int64_t sr = p.a_rows ? p.a_rows[r] : r;
+      src[i] = p.a + sr * K + lseg * 16;
+    } else {
+      src[i] = wbase + DSMOE_WROW(row) * K + lseg * 16;
+    }
+    dst_is_a[i] = is_a;
+    dst_off[i] = jj * 1024;
   }
-  const uint8_t* b_src[C::B_LOADS];
-  int b_lds[C::B_LOADS];
-#pragma unroll
-  for (int i = 0; i < C::B_LOADS; ++i) {
-    const int idx = tid + THREADS * i;
-    const int lc = idx >> 3, seg = idx & 7;
-    b_src[i] = wbase + DSMOE_WROW(lc) * K + seg * 16;
-    b_lds[i] = swz(lc, seg);
+  const float* sa_src;
+  {
+    const int row = wave * C::ROWS_PER_WAVE + (lane < C::ROWS_PER_WAVE ? lane : 0);
+    const int64_t r = row0 + row < row1 ? row0 + row : row0;
+    const int64_t sr = p.a_rows ? p.a_rows[r] : r;
+    sa_src = p.a_scale + sr * kchunks;
   }
-  const float* sa_src = nullptr;
-  if (tid < BM) {
-    const int64_t r = row0 + tid < row1 ? row0 + tid : row0;
-    const int64_t src = p.a_rows ? p.a_rows[r] : r;
-    sa_src = p.a_scale + src * kchunks;
+  // weight-block scales for every chunk, staged once: half hb covers local
+  // columns [128*hb, 128*hb + 128), which sit in one 128-row block of W
+  constexpr int HALVES = BN / 128;
+  for (int64_t i = tid; i < HALVES * kchunks; i += THREADS) {
+    const int hb = static_cast<int>(i / kchunks);
+    const int64_t c = i - hb * kchunks;
+    s_sw[hb][c] = wsbase[(DSMOE_WROW(hb * 128) / BK) * kchunks + c];
   }
-  // this wave's 64 columns sit in one 128-row block of W
-  const float* sw_src = wsbase + (DSMOE_WROW(wn * 64) / BK) * kchunks;
 #undef DSMOE_WROW
+  const int my_half = (wn * 64) / 128;
+  __syncthreads();
 
-  u32x4 ra[C::A_LOADS], rb[C::B_LOADS];
-  float rsa = 0.f;
-  // (plain macros rather than lambdas: a by-reference capture would make the
-  // register arrays addressable and move them to LDS)
-#define DSMOE_GLOAD(cc)                                                                     \
-  do {                                                                                      \
-    _Pragma("unroll") for (int i = 0; i < C::A_LOADS; ++i) ra[i] =                          \
-        *reinterpret_cast<const u32x4*>(a_src[i] + (cc) * BK);                              \
-    _Pragma("unroll") for (int i = 0; i < C::B_LOADS; ++i) rb[i] =                          \
-        *reinterpret_cast<const u32x4*>(b_src[i] + (cc) * BK);                              \
-    if (tid < BM) rsa = sa_src[(cc)];                                                       \
-  } while (0)
-#define DSMOE_SSTORE(bb)                                                                    \
-  do {                                                                                      \
-    _Pragma("unroll") for (int i = 0; i < C::A_LOADS; ++i)                                  \
-        *reinterpret_cast<u32x4*>(&s_a[(bb)][a_lds[i]]) = ra[i];                            \
-    _Pragma("unroll") for (int i = 0; i < C::B_LOADS; ++i)                                  \
-        *reinterpret_cast<u32x4*>(&s_b[(bb)][b_lds[i]]) = rb[i];                            \
-    if (tid < BM) s_sa[(bb)][tid] = rsa;                                                    \
+  const uint32_t a_base = lds_addr(&s_a[0][0]);
+  const uint32_t b_base = lds_addr(&s_b[0][0]);
+  const uint32_t sa_base = lds_addr(&s_sa[0][0]) + 4 * wave * C::ROWS_PER_WAVE;
+#define DSMOE_ISSUE(cc, st)                                                                  \
+  do {                                                                                       \
+    _Pragma("unroll") for (int i = 0; i < C::PER_WAVE; ++i) {                                \
+      const uint32_t base = dst_is_a[i] ? a_base + (st) * (LBM * BK) : b_base + (st) * (BN * BK); \
+      dma_16(src[i] + (cc) * BK, __builtin_amdgcn_readfirstlane(base + dst_off[i]));          \
+    }                                                                                        \
+    if (lane < C::ROWS_PER_WAVE)                                                             \
+      dma_4(sa_src + (cc), __builtin_amdgcn_readfirstlane(sa_base + (st) * (LBM * 4)));       \
   } while (0)
 
   f32x4 acc[4][4];
@@ -198,28 +458,39 @@ __global__ __launch_bounds__(2 * BN) void gemm_kernel(GemmProblem p, int64_t n_t
 
   const int frow = lane & 15;       // row (A) / column (B) inside a 16x16 tile
   const int fseg = (lane >> 4) * 2; // first of the two 16-byte K segments
-  DSMOE_GLOAD(0);
-  DSMOE_SSTORE(0);
-  __syncthreads();
+
+  // prologue: stages 0 .. S-2 in flight
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < kchunks) DSMOE_ISSUE(st, st);
+
   for (int64_t c = 0; c < kchunks; ++c) {
-    const int buf = static_cast<int>(c & 1);
-    if (c + 1 < kchunks) DSMOE_GLOAD(c + 1);
-    const float sw = sw_src[c];
+    const int buf = static_cast<int>(c % S);
+    // chunk c has landed once at most (stages issued after it) * LPS of this
+    // wave's copies are still outstanding
+    const int64_t after = min<int64_t>(S - 2, kchunks - 1 - c);
+    if (after >= 2)
+      wait_vmcnt<2 * C::LPS>();
+    else if (after == 1)
+      wait_vmcnt<C::LPS>();
+    else
+      wait_vmcnt<0>();
+    block_barrier();  // every wave's copies landed; every wave is done with chunk c-1
+    if (c + S - 1 < kchunks) DSMOE_ISSUE(c + S - 1, static_cast<int>((c + S - 1) % S));
+    const float sw = s_sw[my_half][c];
 
     i32x8 af[4], bfr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 64 + i * 16 + frow;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(&s_a[buf][swz(r, fseg)]);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(&s_a[buf][swz(r, fseg + 1)]);
-      af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      af[i] = cat8(*reinterpret_cast<const u32x4*>(&s_a[buf][swz(r, fseg)]),
+                   *reinterpret_cast<const u32x4*>(&s_a[buf][swz(r, fseg + 1)]));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = wn * 64 + j * 16 + frow;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(&s_b[buf][swz(r, fseg)]);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(&s_b[buf][swz(r, fseg + 1)]);
-      bfr[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      bfr[j] = cat8(*reinterpret_cast<const u32x4*>(&s_b[buf][swz(r, fseg)]),
+                    *reinterpret_cast<const u32x4*>(&s_b[buf][swz(r, fseg + 1)]));
     }
     float scl[4][4];
 #pragma unroll
@@ -236,141 +507,248 @@ __global__ __launch_bounds__(2 * BN) void gemm_kernel(GemmProblem p, int64_t n_t
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(part[r], scl[i][r], acc[i][j][r]);
       }
-    if (c + 1 < kchunks) DSMOE_SSTORE(buf ^ 1);
-    __syncthreads();
   }
-#undef DSMOE_GLOAD
-#undef DSMOE_SSTORE
+#undef DSMOE_ISSUE
+  __syncthreads();  // all waves are done with the staging buffers (epilogues reuse them)
 
-  // ------------------------------------------------------------------ epilogues
-  // lane (i, j, r) holds output row  wm*64 + 16i + 4*(lane/16) + r
-  //                       and column wn*64 + 16j + lane%16
   if constexpr (EPI == Epilogue::kStore || EPI == Epilogue::kGateStore) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = row0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-        if (row >= row1) continue;
-        float gsc = 1.0f;
-        if constexpr (EPI == Epilogue::kGateStore) gsc = p.row_gate[row];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t col = nt * BN + wn * 64 + j * 16 + frow;
-          float v = acc[i][j][r];
-          if constexpr (EPI == Epilogue::kGateStore) v = v * gsc;
-          if (p.c_f32)
-            static_cast<float*>(p.c)[row * N + col] = v;
-          else
-            static_cast<uint16_t*>(p.c)[row * N + col] = f32_to_bf16(v);
-        }
-      }
+    epi_store<4, 4, EPI>(p, acc, row0, row1, wm * 64, nt * BN + wn * 64);
   } else if constexpr (EPI == Epilogue::kCombine) {
-    const int32_t K_ = p.topk;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = row0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-        if (row >= row1) continue;
-        const int64_t tok = row - p.row_base;
-        const int32_t* inv_t = p.inv + tok * K_;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t col = nt * BN + wn * 64 + j * 16 + frow;
-          float v = acc[i][j][r];
-          for (int k = 0; k < K_; ++k) {
-            const int64_t orow = inv_t[k];
-            if (p.c_f32)
-              v = v + static_cast<const float*>(p.o_routed)[orow * N + col];
-            else
-              v = v + bf16_to_f32(static_cast<const uint16_t*>(p.o_routed)[orow * N + col]);
-          }
-          if (p.c_f32)
-            static_cast<float*>(p.c)[tok * N + col] = v;
-          else
-            static_cast<uint16_t*>(p.c)[tok * N + col] = f32_to_bf16(v);
-        }
-      }
-  } else {  // kSwiGLUQuant: waves 0,1 (per M half) hold gate columns, 2,3 up columns
-    float* s_up = reinterpret_cast<float*>(&s_b[0][0]);          // [128][128] f32 = 64 KB
-    float* s_rmax = reinterpret_cast<float*>(&s_a[0][0]);        // [2][128]
-    uint8_t* s_code = &s_a[1][0];                                // [128][128] bytes
-    if (wn >= 2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int lr = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-            const int lc = (wn - 2) * 64 + j * 16 + frow;
-            s_up[lr * 128 + lc] = acc[i][j][r];
-          }
-    }
-    __syncthreads();
-    float av[4][4][4];
-    if (wn < 2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int lr = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-          float m = 0.f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int lc = wn * 64 + j * 16 + frow;
-            const float gt = acc[i][j][r];
-            const float up = s_up[lr * 128 + lc];
-            const float a = gt / (1.0f + expf(-gt)) * up;
-            av[i][j][r] = a;
-            m = fmaxf(m, fabsf(a));
-          }
-          m = wave_max_width(m, 16);
-          if (frow == 0) s_rmax[wn * 128 + lr] = m;
-        }
-    }
-    __syncthreads();
-    if (wn < 2) {
-      const int64_t I = N / 2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int lr = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-          const float amax = fmaxf(s_rmax[lr], s_rmax[128 + lr]);
-          const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int lc = wn * 64 + j * 16 + frow;
-            s_code[lr * 128 + lc] = static_cast<uint8_t>(e4m3_encode(av[i][j][r] / s));
-          }
-          const int64_t row = row0 + lr;
-          if (wn == 0 && frow == 0 && row < row1) p.c_scale[row * (I / BK) + nt] = s;
-        }
-    }
-    __syncthreads();
-    // coalesced code store: 128 rows x 128 bytes, 16 bytes per thread per step
-    const int64_t I = N / 2;
-    for (int idx = tid; idx < BM * 8; idx += THREADS) {
-      const int lr = idx >> 3, seg = idx & 7;
-      const int64_t row = row0 + lr;
-      if (row < row1)
-        *reinterpret_cast<uint4*>(static_cast<uint8_t*>(p.c) + row * I + nt * 128 + seg * 16) =
-            *reinterpret_cast<const uint4*>(&s_code[lr * 128 + seg * 16]);
-    }
+    epi_combine<4, 4>(p, acc, row0, row1, wm * 64, nt * BN + wn * 64,
+                      reinterpret_cast<float*>(&s_a[0][0]) + wave * 16 * 64);
+  } else {  // waves with wn 0,1 hold gate columns, 2,3 the matching up columns
+    epi_swiglu<4, 4, LBM, 2>(p, acc, row0, row1, wm * 64, wn < 2, wn & 1, (wn & 1) * 64, nt,
+                             reinterpret_cast<float*>(&s_b[0][0]),
+                             reinterpret_cast<float*>(&s_sa[0][0]), &s_a[1][0]);
   }
 }
 
+// ===========================================================================
+// gemm_ws_kernel: weight streaming for groups of few rows
+// ===========================================================================
+template <int BM>
+struct WsCfg {
+  static constexpr int NW = 8;
+  static constexpr int THREADS = 512;
+  static constexpr int BN = 256;                 // 8 waves x 32 columns
+  static constexpr int NI = BM / 16;             // row tiles per wave
+  static constexpr int D = 3;                    // W chunks loaded ahead
+  static constexpr int SLOTS = D + 1;            // W register sets
+  static constexpr int A_SEGS = BM * 8;          // 16-byte segments of one A chunk
+  static constexpr int A_PER = (A_SEGS + THREADS - 1) / THREADS;
+  // LDS: two A stages + scales during the K loop; the SwiGLU epilogue reuses
+  // it for the up half (f32), the row maxima and the codes
+  static constexpr int MAIN_BYTES = 2 * BM * BK + 2 * BM * 4;
+  static constexpr int EPI_BYTES = BM * 128 * 4 + 4 * BM * 4 + BM * 128;
+  static constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+};
+
+template <int BM, Epilogue EPI>
+__global__ __launch_bounds__(512) void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
+  using C = WsCfg<BM>;
+  constexpr int NI = C::NI;
+  constexpr int SLOTS = C::SLOTS;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_raw[C::LDS_BYTES];
+  __shared__ float s_sw[2][kMaxChunks];
+  __shared__ int64_t s_scan[C::NW];
+  __shared__ int64_t s_tile[4];
+  uint8_t* s_a = s_raw;                                               // [2][BM*BK]
+  float* s_sa = reinterpret_cast<float*>(s_raw + 2 * BM * BK);         // [2][BM]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int64_t logical = xcd_logical_block();
+  if (!decode_tile<C::THREADS, BM>(p.offsets, p.G, logical, n_tiles, s_scan, s_tile)) return;
+  const int32_t g = static_cast<int32_t>(s_tile[0]);
+  const int64_t nt = s_tile[3];
+  const int64_t row0 = s_tile[1];
+  const int64_t row1 = min(s_tile[2], p.row_limit);
+  if (row0 >= row1) return;
+
+  const int64_t K = p.K, N = p.N;
+  const int64_t kchunks = K / BK;
+  const bool last = (p.w_last != nullptr) && (g == p.G - 1);
+  const uint8_t* wbase = last ? p.w_last : p.w + static_cast<int64_t>(g) * N * K;
+  const float* wsbase = last ? p.w_scale_last : p.w_scale + static_cast<int64_t>(g) * (N / BK) * kchunks;
+  const int64_t w_row_base = (EPI == Epilogue::kSwiGLUQuant) ? nt * 128 : nt * C::BN;
+  const int64_t w_up_shift = (EPI == Epilogue::kSwiGLUQuant) ? N / 2 - 128 : 0;
+#define DSMOE_WROW(lc) (w_row_base + (lc) + ((lc) >= 128 ? w_up_shift : 0))
+
+  // this wave's W columns: local [32*wave, 32*wave + 32), two 16-column
+  // tiles; lane reads row 16j + lane%16, bytes 32*(lane/16) .. +32 of a chunk
+  const uint8_t* wsrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    wsrc[j] = wbase + DSMOE_WROW(wave * 32 + j * 16 + (lane & 15)) * K + (lane >> 4) * 32;
+  // A: BM rows x 8 segments per chunk, A_PER segments per thread
+  const uint8_t* asrc[C::A_PER];
+  int adst[C::A_PER];
+  bool aval[C::A_PER];
+#pragma unroll
+  for (int i = 0; i < C::A_PER; ++i) {
+    const int idx = tid + C::THREADS * i;
+    aval[i] = idx < C::A_SEGS;
+    const int lr = aval[i] ? idx >> 3 : 0, seg = idx & 7;
+    const int64_t r = row0 + lr < row1 ? row0 + lr : row0;
+    const int64_t sr = p.a_rows ? p.a_rows[r] : r;
+    asrc[i] = p.a + sr * K + seg * 16;
+    adst[i] = swz(lr, seg);
+  }
+  // (threads past the tile load a valid row too: the loads stay unconditional,
+  // which keeps the rotating register sets free of merge copies)
+  const float* sasrc;
+  {
+    const int lr = tid < BM ? tid : 0;
+    const int64_t r = row0 + lr < row1 ? row0 + lr : row0;
+    const int64_t sr = p.a_rows ? p.a_rows[r] : r;
+    sasrc = p.a_scale + sr * kchunks;
+  }
+  for (int64_t i = tid; i < 2 * kchunks; i += C::THREADS) {
+    const int hb = static_cast<int>(i / kchunks);
+    const int64_t c = i - hb * kchunks;
+    s_sw[hb][c] = wsbase[(DSMOE_WROW(hb * 128) / BK) * kchunks + c];
+  }
+  const int my_half = (wave * 32) / 128;
+#undef DSMOE_WROW
+
+  u32x4 wr[SLOTS][2][2];
+  u32x4 ra[C::A_PER];
+  float rsa = 0.f;
+#define DSMOE_WLOAD(cc, slot)                                                                \
+  do {                                                                                       \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                          \
+      wr[slot][j][0] = *reinterpret_cast<const u32x4*>(wsrc[j] + (cc) * BK);                 \
+      wr[slot][j][1] = *reinterpret_cast<const u32x4*>(wsrc[j] + (cc) * BK + 16);            \
+    }                                                                                        \
+  } while (0)
+#define DSMOE_ALOAD(cc)                                                                      \
+  do {                                                                                       \
+    _Pragma("unroll") for (int i = 0; i < C::A_PER; ++i) ra[i] =                             \
+        *reinterpret_cast<const u32x4*>(asrc[i] + (cc) * BK);                                \
+    rsa = sasrc[(cc)];                                                                       \
+  } while (0)
+#define DSMOE_ASTORE(bb)                                                                     \
+  do {                                                                                       \
+    _Pragma("unroll") for (int i = 0; i < C::A_PER; ++i) if (aval[i])                       \
+        *reinterpret_cast<u32x4*>(&s_a[(bb) * BM * BK + adst[i]]) = ra[i];                   \
+    if (tid < BM) s_sa[(bb) * BM + tid] = rsa;                                               \
+  } while (0)
+
+  f32x4 acc[NI][2];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int frow = lane & 15;
+  const int fseg = (lane >> 4) * 2;
+
+  // prologue: W chunks 0 .. D-1 in flight, A chunk 0 staged
+#pragma unroll
+  for (int d = 0; d < C::D; ++d) DSMOE_WLOAD(min<int64_t>(d, kchunks - 1), d);
+  DSMOE_ALOAD(0);
+  DSMOE_ASTORE(0);
+  __syncthreads();
+
+  for (int64_t c0 = 0; c0 < kchunks; c0 += SLOTS) {
+#pragma unroll
+    for (int u = 0; u < SLOTS; ++u) {
+      const int64_t c = c0 + u;
+      // loads are issued unconditionally (clamped to the last chunk) so every
+      // register set is written on every path
+      DSMOE_ALOAD(min<int64_t>(c + 1, kchunks - 1));
+      DSMOE_WLOAD(min<int64_t>(c + C::D, kchunks - 1), (u + C::D) % SLOTS);
+      if (c < kchunks) {
+        const int buf = static_cast<int>(c & 1);
+        const float sw = s_sw[my_half][c];
+        const i32x8 b0 = cat8(wr[u][0][0], wr[u][0][1]);
+        const i32x8 b1 = cat8(wr[u][1][0], wr[u][1][1]);
+        // software pipeline over the row tiles: the MFMAs of tile i are in
+        // flight while tile i-1 is promoted; the scheduling barriers keep the
+        // compiler from hoisting every tile's operands at once (register
+        // pressure)
+        f32x4 pp0 = {0.f, 0.f, 0.f, 0.f}, pp1 = {0.f, 0.f, 0.f, 0.f}, psa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i <= NI; ++i) {
+          f32x4 p0, p1, sa4;
+          if (i < NI) {
+            const int r = i * 16 + frow;
+            const i32x8 af = cat8(*reinterpret_cast<const u32x4*>(&s_a[buf * BM * BK + swz(r, fseg)]),
+                                  *reinterpret_cast<const u32x4*>(&s_a[buf * BM * BK + swz(r, fseg + 1)]));
+            sa4 = *reinterpret_cast<const f32x4*>(&s_sa[buf * BM + i * 16 + (lane >> 4) * 4]);
+            p0 = mfma_chunk(af, b0);
+            p1 = mfma_chunk(af, b1);
+          }
+          if (i > 0) {
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) {
+              const float scl = psa[r2] * sw;
+              acc[i - 1][0][r2] = __builtin_fmaf(pp0[r2], scl, acc[i - 1][0][r2]);
+              acc[i - 1][1][r2] = __builtin_fmaf(pp1[r2], scl, acc[i - 1][1][r2]);
+            }
+            // pin the promotion here (otherwise it is sunk to the loop end and
+            // every tile's partial sums stay live at once)
+            asm volatile("" : "+v"(acc[i - 1][0]), "+v"(acc[i - 1][1]));
+          }
+          if (i < NI) {
+            pp0 = p0;
+            pp1 = p1;
+            psa = sa4;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      DSMOE_ASTORE(static_cast<int>((c + 1) & 1));
+      __syncthreads();
+    }
+  }
+#undef DSMOE_WLOAD
+#undef DSMOE_ALOAD
+#undef DSMOE_ASTORE
+
+  if constexpr (EPI == Epilogue::kStore || EPI == Epilogue::kGateStore) {
+    epi_store<NI, 2, EPI>(p, acc, row0, row1, 0, nt * C::BN + wave * 32);
+  } else if constexpr (EPI == Epilogue::kCombine) {
+    epi_combine<NI, 2>(p, acc, row0, row1, 0, nt * C::BN + wave * 32,
+                       reinterpret_cast<float*>(s_raw) + wave * 16 * 32);
+  } else {  // waves 0-3 hold gate columns 32w.., waves 4-7 the matching up columns
+    epi_swiglu<NI, 2, BM, 4>(p, acc, row0, row1, 0, wave < 4, wave & 3, (wave & 3) * 32, nt,
+                             reinterpret_cast<float*>(s_raw),
+                             reinterpret_cast<float*>(s_raw + BM * 128 * 4),
+                             s_raw + BM * 128 * 4 + 4 * BM * 4);
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <int BN, Epilogue EPI>
-hipError_t launch_cfg(const GemmProblem& p, hipStream_t s) {
+hipError_t launch_lds(const GemmProblem& p, hipStream_t s) {
   const int64_t n_tiles = (EPI == Epilogue::kSwiGLUQuant) ? (p.N / 2) / 128 : p.N / BN;
-  const int64_t m_tiles_ub = (p.M_total + BM - 1) / BM + p.G;
-  int64_t blocks = m_tiles_ub * n_tiles;
-  blocks = (blocks + kXcds - 1) / kXcds * kXcds;
+  const int64_t blocks = pad_grid(((p.M_total + LBM - 1) / LBM + p.G) * n_tiles);
   if (blocks == 0) return hipSuccess;
-  gemm_kernel<BN, EPI><<<dim3(static_cast<unsigned>(blocks)), Kcfg<BN, EPI>::THREADS, 0, s>>>(p, n_tiles);
+  gemm_lds_kernel<BN, EPI><<<dim3(static_cast<unsigned>(blocks)), LdsCfg<BN>::THREADS, 0, s>>>(p, n_tiles);
   return hipGetLastError();
+}
+
+template <int BM, Epilogue EPI>
+hipError_t launch_ws(const GemmProblem& p, hipStream_t s) {
+  const int64_t n_tiles = (EPI == Epilogue::kSwiGLUQuant) ? (p.N / 2) / 128 : p.N / 256;
+  const int64_t blocks = pad_grid(((p.M_total + BM - 1) / BM + p.G) * n_tiles);
+  if (blocks == 0) return hipSuccess;
+  gemm_ws_kernel<BM, EPI><<<dim3(static_cast<unsigned>(blocks)), 512, 0, s>>>(p, n_tiles);
+  return hipGetLastError();
+}
+
+template <Epilogue EPI>
+hipError_t launch_ws_bm(const GemmProblem& p, int bm, hipStream_t s) {
+  switch (bm) {
+    case 16: return launch_ws<16, EPI>(p, s);
+    case 32: return launch_ws<32, EPI>(p, s);
+    case 64: return launch_ws<64, EPI>(p, s);
+    case 128: return launch_ws<128, EPI>(p, s);
+    default: return launch_ws<192, EPI>(p, s);
+  }
 }
 
 // y[t][n] = sum over k of o[inv[t][k]][n] (layers without a shared expert);
@@ -415,17 +793,41 @@ hipError_t launch_combine(const void* o, const int32_t* inv, int64_t T, int32_t 
   return hipGetLastError();
 }
 
+// Row-tile height of the weight-streaming kernel for groups of about
+// `rows` rows (0: use the 128-row LDS kernel).  A tile that holds a whole
+// group keeps every weight byte to a single HBM read; the mean group size
+// is padded by half to cover its spread.  Taller groups go to the LDS
+// kernel, whose 128 x BN tiles reuse each staged weight chunk over more rows.
+int ws_tile_rows(int64_t rows_hint) {
+  const int64_t want = rows_hint + rows_hint / 2;
+  for (int bm : {16, 32, 64, 128, 192})
+    if (want <= bm) return bm;
+  return 0;
+}
+
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t s) {
   if (p.M_total == 0) return hipSuccess;
+  const bool wide = p.N % 256 == 0;   // 256-column tiles (8 waves) when N allows
+  const int bm = (wide || p.epi == Epilogue::kSwiGLUQuant) ? ws_tile_rows(p.rows_hint) : 0;
+  if (bm > 0) {
+    switch (p.epi) {
+      case Epilogue::kStore: return launch_ws_bm<Epilogue::kStore>(p, bm, s);
+      case Epilogue::kGateStore: return launch_ws_bm<Epilogue::kGateStore>(p, bm, s);
+      case Epilogue::kCombine: return launch_ws_bm<Epilogue::kCombine>(p, bm, s);
+      case Epilogue::kSwiGLUQuant: return launch_ws_bm<Epilogue::kSwiGLUQuant>(p, bm, s);
+    }
+  }
   switch (p.epi) {
     case Epilogue::kStore:
-      return launch_cfg<128, Epilogue::kStore>(p, s);
+      return wide ? launch_lds<256, Epilogue::kStore>(p, s) : launch_lds<128, Epilogue::kStore>(p, s);
     case Epilogue::kGateStore:
-      return launch_cfg<128, Epilogue::kGateStore>(p, s);
+      return wide ? launch_lds<256, Epilogue::kGateStore>(p, s)
+                  : launch_lds<128, Epilogue::kGateStore>(p, s);
     case Epilogue::kCombine:
-      return launch_cfg<128, Epilogue::kCombine>(p, s);
+      return wide ? launch_lds<256, Epilogue::kCombine>(p, s)
+                  : launch_lds<128, Epilogue::kCombine>(p, s);
     case Epilogue::kSwiGLUQuant:
-      return launch_cfg<256, Epilogue::kSwiGLUQuant>(p, s);
+      return launch_lds<256, Epilogue::kSwiGLUQuant>(p, s);
   }
   return hipErrorInvalidValue;
 }

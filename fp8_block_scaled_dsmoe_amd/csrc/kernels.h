@@ -61,6 +61,7 @@ struct GemmProblem {
   int32_t topk;              // kCombine
   int64_t row_base;          // kCombine: output row r is token r - row_base
   int64_t row_limit;         // rows >= row_limit are never read or written
+  int64_t rows_hint;         // typical rows per group (selects the kernel shape)
 };
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t s);

@@ -158,7 +158,7 @@ dsmoe_status dsmoe_route(const float* logits, const float* bias, int64_t T, int3
  * (sum over k in chunk j of a[ar][k] * w[g][n][k]), ar = a_rows ? a_rows[r] : r.
  * G = 1 with offsets = {0, M} is the dense GEMM.  The group sizes are read
  * on the device; the host never synchronises.
- * Requires N % 128 == 0, K % 128 == 0, 1 <= G, M_total >= 0.
+ * Requires N % 128 == 0, K % 128 == 0, K <= 32768, 1 <= G, M_total >= 0.
  */
 dsmoe_status dsmoe_fp8_grouped_gemm(const uint8_t* a, const float* a_scale,
                                     const int32_t* a_rows, const int32_t* offsets, int32_t G,
@@ -169,7 +169,7 @@ dsmoe_status dsmoe_fp8_grouped_gemm(const uint8_t* a, const float* a_scale,
  * Layer description.  Source: V3 notes §2 (one shared expert, 256 routed
  * experts of intermediate size 2048, 8 chosen) and §4.2 (at most 4 of 8
  * nodes).  H hidden size, I expert intermediate size (both multiples of
- * 128), E routed experts in G groups, Mg groups kept, K experts chosen,
+ * 128, at most 32768), E routed experts in G groups, Mg groups kept, K experts chosen,
  * n_shared shared experts (0 or 1; intermediate size I, gate 1).
  */
 typedef struct dsmoe_moe_desc {

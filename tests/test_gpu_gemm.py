@@ -124,3 +124,31 @@ def test_dense_full_size_sampled_rows(dt):
     want = og.block_scaled_gemm(qa, sa, qw, sw)
     dn = og.gemm_normaliser(qa, sa, qw, sw)
     assert_normalised_close(host(c)[rows], want, dn, TOL[dt], f"dense full size {dt}")
+
+
+@pytest.mark.parametrize("mean_rows", [3, 12, 30, 70, 120, 400])
+def test_grouped_tile_shapes(mean_rows):
+    """Group sizes around each row-tile height the library picks (weight
+    streaming with 16..192-row tiles, and the 128-row LDS kernel), including
+    empty groups and groups longer than one tile."""
+    d = _dsmoe()
+    r = np.random.default_rng(mean_rows)
+    G, N, K = 7, 512, 384
+    sizes = r.poisson(mean_rows, size=G)
+    sizes[1] = 0
+    sizes[3] = 3 * mean_rows + 17
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    m_total = int(offsets[-1])
+    rows_a = max(m_total, 1)
+    qa = _codes(r, (rows_a, K))
+    sa = (np.ldexp(1.0, r.integers(-8, -2, size=(rows_a, K // 128))) *
+          r.uniform(1, 2, size=(rows_a, K // 128))).astype(np.float32)
+    qw = _codes(r, (G, N, K))
+    sw = np.ldexp(1.0, r.integers(-12, -6, size=(G, N // 128, K // 128))).astype(np.float32)
+    a_rows = r.permutation(rows_a)[:m_total].astype(np.int32)
+    banner(f"gemm grouped tile shapes mean_rows={mean_rows} sizes={sizes.tolist()}")
+    for dt in (torch.float32, torch.bfloat16):
+        c = d.fp8_grouped_gemm(dev(qa), dev(sa), dev(offsets), dev(qw), dev(sw), a_rows=dev(a_rows),
+                               out_dtype=dt)
+        want, dn = og.grouped_gemm(qa, sa, a_rows, offsets, qw, sw)
+        assert_normalised_close(host(c), want, dn, TOL[dt], f"grouped mean {mean_rows} {dt}")
