@@ -41,8 +41,48 @@ def parse():
                     choices=["v3_prefill", "v3_decode", "v3_skew", "tiny"])
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=10)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (3 times): the known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm1_swiglu_v3_prefill.json")
+GEMM_SOURCES = ["gemm.hip", "common.h", "kernels.h"]
+
+
+def gemm_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "fp8_block_scaled_dsmoe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the gate/up GEMM from the committed counter runs,
+    or None when they were taken on other kernel sources or another workload."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except OSError:
+        return None
+    if t.get("workload") != workload or t.get("gemm_sources_sha256") != gemm_sources_sha256():
+        return None
+    return int(t["traffic_bytes_per_launch"])
+
+
+def copy_calibration(torch):
+    src = torch.empty((COPY_BYTES,), dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
 
 
 def build_layer(cfg, d, torch, dsi):
@@ -98,17 +138,23 @@ def cpu_baseline(cfg, n_tokens, torch, dsi):
     z, _ = ol.router_logits(xs, inp["router_w"])
     r = orr.route(z.astype(np.float32), inp["bias"], cfg.G, cfg.Mg, cfg.K)
     needed = sorted(set(r["topk_idx"].reshape(-1).tolist()) | {cfg.E})
-    cache = {}
+    full = dsi.layer_inputs_host(cfg, 0) if cfg.name == "tiny" else None
+    host_w = {}
     for e in needed:
-        if cfg.name == "tiny":
-            full = dsi.layer_inputs_host(cfg, 0)
-            a, b = full["w13"][e], full["w2"][e]
+        if full is not None:
+            host_w[e] = (full["w13"][e], full["w2"][e])
         else:
             at, bt = dsi.expert_weights_device(cfg, e, "cuda")
-            a, b = at.float().cpu().numpy(), bt.float().cpu().numpy()
-        q13, s13 = oq.quant_w_128x128(a)
-        q2, s2 = oq.quant_w_128x128(b)
-        cache[e] = (q13, s13, q2, s2)
+            host_w[e] = (at.float().cpu().numpy(), bt.float().cpu().numpy())
+
+    def quant(e):
+        a, b = host_w.pop(e)
+        return e, oq.quant_w_128x128(a) + oq.quant_w_128x128(b)
+
+    from concurrent.futures import ThreadPoolExecutor
+    log(f"cpu baseline: quantising {len(needed)} experts on the host (untimed)")
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as pool:
+        cache = dict(pool.map(quant, needed))
     log(f"cpu baseline: oracle on {n_tokens} tokens, {len(needed)} experts")
     t0 = time.perf_counter()
     ol.moe_layer(xs, inp["router_w"], inp["bias"], lambda e: cache[e], cache[cfg.E], cfg.G, cfg.Mg, cfg.K)
@@ -128,6 +174,9 @@ def main():
               "(this build has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     import fp8_block_scaled_dsmoe_amd as d
     import dsmoe_inputs as dsi
 
@@ -213,8 +262,9 @@ def main():
                                f"1 shared expert, I={I}, y {args.out_dtype}",
                    "T": T, "H": H, "E": E, "G": cfg.G, "Mg": cfg.Mg, "K": K, "I": I},
         "roofline": {"bound": g1_bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": "gemm_kernel<256, SwiGLU-requant> (gate/up GEMM)",
+                     "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(cfg.name),
+                     "kernel": "gate/up grouped FP8 GEMM + SwiGLU + 1x128 requant (one launch)",
                      "algorithmic_bytes": int(g1_bytes), "algorithmic_flops": g1_flops,
                      "avg_ms": round(g1_ms, 4)},
         "grouped_gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2),

@@ -269,24 +269,24 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
 
   DSMOE_MARK(0);
 
-  // a1: 1x128 quantisation of x
+  // 1x128 quantisation of x
   DSMOE_TRY(dsmoe::launch_quant_act(x, false, T, H, qx, sx, st));
   DSMOE_MARK(1);
-  // a3: router logits (bf16 MFMA, FP32 accumulation)
+  // router logits (bf16 MFMA, FP32 accumulation)
   DSMOE_TRY(dsmoe::launch_router_logits(static_cast<const uint16_t*>(x),
                                         static_cast<const uint16_t*>(w->router_w), T, H, E,
                                         logits, st));
   DSMOE_MARK(2);
-  // a4: routing
+  // group-limited top-K routing
   DSMOE_TRY(dsmoe::launch_route_select(logits, bias, T, E, d->G, d->Mg, K, topk, gates,
                                        counts_out, st));
   DSMOE_MARK(3);
-  // a5: counts -> offsets, permutation, inverse, per-row gates; shared rows
+  // counts -> offsets, permutation, inverse, per-row gates; shared rows
   DSMOE_TRY(dsmoe::launch_permute(topk, gates, T, E, K, counts_out, offsets, perm, inv, row_gate,
                                   d->n_shared ? offsets_ext : nullptr, st));
   DSMOE_MARK(4);
 
-  // a6 + a7 (+ a9 first half): gate/up GEMM with SwiGLU and 1x128 requant
+  // gate/up GEMM of every routed expert and the shared one, SwiGLU and 1x128 requant
   dsmoe::GemmProblem g1{};
   g1.a = qx;
   g1.a_scale = sx;
@@ -308,7 +308,7 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
   DSMOE_TRY(dsmoe::launch_grouped_gemm(g1, st));
   DSMOE_MARK(5);
 
-  // a8: routed down projection, scaled by the gate
+  // routed down projection, scaled by the gate
   dsmoe::GemmProblem g2{};
   g2.a = qa;
   g2.a_scale = sa;
@@ -330,7 +330,7 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
   DSMOE_MARK(6);
 
   if (d->n_shared) {
-    // a9 (down projection of the shared expert) + a10 combine in its epilogue
+    // down projection of the shared expert, with the combine in its epilogue
     dsmoe::GemmProblem g3{};
     g3.a = qa;
     g3.a_scale = sa;

@@ -158,3 +158,18 @@ def test_requant_slack_flags_codes_at_midpoints_only():
     # a large error bound makes every non-zero element ambiguous
     _, n_all = layer.requant_slack(h + 1.0, np.ones((1, 256)) * 1e3, a, qa, sa, q2, s2, 1.0)
     assert n_all == 128
+
+
+def test_router_logits_one_hot_rows_pick_router_columns():
+    # x rows that are -2 times a unit vector e_h give z[t][e] = -2 Wr[e][h]
+    # exactly, and normaliser 2 |Wr[e][h]|; a transposed operand or a dropped
+    # absolute value fails this.
+    E, H = 6, 256
+    wr = normal_bf16("pin_wr", (E, H), 0.3, seed=1)
+    hs = np.array([0, 5, 127, 128, 255])
+    x = np.zeros((len(hs), H), np.float32)
+    x[np.arange(len(hs)), hs] = -2.0
+    z, dz = layer.router_logits(x, wr)
+    assert z.shape == (len(hs), E)
+    assert np.array_equal(z, -2.0 * wr[:, hs].T.astype(np.float64))
+    assert np.array_equal(dz, 2.0 * np.abs(wr[:, hs].T).astype(np.float64))
