@@ -44,7 +44,13 @@ constexpr int BK = 128;
 constexpr int kXcds = 8;
 constexpr int kMaxChunks = 256;   // K <= 32768
 
-__device__ __forceinline__ int swz(int row, int seg) { return row * BK + ((seg ^ (row & 7)) << 4); }
+// LDS tiles hold 128-byte rows of 8 16-byte segments; segment seg of row
+// `row` is stored in slot seg ^ swz_key(row).  MFMA operand reads have 16
+// lanes read 16 rows (one segment each): the key is distinct over any 8
+// consecutive rows and over the 8 even (8 odd) rows of a 16-row tile, so the
+// reads spread over all banks whether a read cycle serves 8 or 16 lanes.
+__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int seg) { return row * BK + ((seg ^ swz_key(row)) << 4); }
 
 __device__ __forceinline__ f32x4 mfma_chunk(const i32x8& a, const i32x8& b) {
   // cbsz = blgp = 0 selects FP8 E4M3 for both operands; zero scale operands
@@ -396,7 +402,7 @@ __global__ __launch_bounds__(2 * BN) void gemm_lds_kernel(GemmProblem p, int64_t
 
   // This wave's share of every chunk: PER_WAVE wave-loads of 1 KB (8 tile
   // rows each, lane -> row 8j + lane/8, physical segment lane%8 holding the
-  // logical K segment (lane%8) ^ (row%8), which realises the XOR swizzle)
+  // logical K segment (lane%8) ^ swz_key(row), which realises the swizzle)
   // plus the 1x128 scales of ROWS_PER_WAVE tile rows.
   const uint8_t* src[C::PER_WAVE];
   uint32_t dst_off[C::PER_WAVE];
@@ -407,7 +413,7 @@ __global__ __launch_bounds__(2 * BN) void gemm_lds_kernel(GemmProblem p, int64_t
     const bool is_a = j < C::A_WLOADS;
     const int jj = is_a ? j : j - C::A_WLOADS;
     const int row = jj * 8 + (lane >> 3);
-    const int lseg = (lane & 7) ^ (row & 7);
+    const int lseg = (lane & 7) ^ swz_key(row);
     if (is_a) {
       const int64_t r = row0 + row < row1 ? row0 + row : row0;
       const int64_t sr = p.a_rows ? p.a_rows[r] : r;
@@ -533,12 +539,17 @@ struct WsCfg {
   static constexpr int BN = 256;                 // 8 waves x 32 columns
   static constexpr int NI = BM / 16;             // row tiles per wave
   static constexpr int D = 3;                    // W chunks loaded ahead
+  // A chunks are loaded A_SETS ahead.  Two sets keep the wait for the next A
+  // chunk from draining the weight stream (see the main loop); small tiles
+  // keep one set so that their register count allows four waves per SIMD
+  // (two blocks per CU), which doubles their weight bytes in flight instead.
+  static constexpr int A_SETS = BM >= 64 ? 2 : 1;
   static constexpr int SLOTS = D + 1;            // W register sets
   static constexpr int A_SEGS = BM * 8;          // 16-byte segments of one A chunk
   static constexpr int A_PER = (A_SEGS + THREADS - 1) / THREADS;
-  // LDS: two A stages + scales during the K loop; the SwiGLU epilogue reuses
-  // it for the up half (f32), the row maxima and the codes
-  static constexpr int MAIN_BYTES = 2 * BM * BK + 2 * BM * 4;
+  // LDS: two A stages + the two halves' row scales during the K loop; the
+  // SwiGLU epilogue reuses it for the up half (f32), the row maxima and the codes
+  static constexpr int MAIN_BYTES = 2 * BM * BK + 2 * 2 * BM * 4;
   static constexpr int EPI_BYTES = BM * 128 * 4 + 4 * BM * 4 + BM * 128;
   static constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
 };
@@ -553,7 +564,8 @@ __global__ __launch_bounds__(512) void gemm_ws_kernel(GemmProblem p, int64_t n_t
   __shared__ int64_t s_scan[C::NW];
   __shared__ int64_t s_tile[4];
   uint8_t* s_a = s_raw;                                               // [2][BM*BK]
-  float* s_sa = reinterpret_cast<float*>(s_raw + 2 * BM * BK);         // [2][BM]
+  // per stage and 128-column half: sa[row][chunk] * sw[half][chunk]
+  float* s_scl = reinterpret_cast<float*>(s_raw + 2 * BM * BK);        // [2][2][BM]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -613,9 +625,17 @@ __global__ __launch_bounds__(512) void gemm_ws_kernel(GemmProblem p, int64_t n_t
   const int my_half = (wave * 32) / 128;
 #undef DSMOE_WROW
 
+  // Register sets: W chunks rotate through SLOTS sets (D ahead), A chunks
+  // through A_SETS sets.  Loads of a wave complete in order, so the wait for
+  // A(c+1) before it is stored to LDS at the end of iteration c also waits for
+  // every load issued before it.  With two A sets, A(c+1) was issued in
+  // iteration c-1, right after W(c+1), and W(c+2), W(c+3) stay in flight
+  // across the barrier; with one set it was issued in iteration c, after
+  // W(c+2), and only W(c+3) does.
+  constexpr int AS = C::A_SETS;
   u32x4 wr[SLOTS][2][2];
-  u32x4 ra[C::A_PER];
-  float rsa = 0.f;
+  u32x4 ra[AS][C::A_PER];
+  float rsa[AS];
 #define DSMOE_WLOAD(cc, slot)                                                                \
   do {                                                                                       \
     _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                          \
@@ -623,17 +643,20 @@ __global__ __launch_bounds__(512) void gemm_ws_kernel(GemmProblem p, int64_t n_t
       wr[slot][j][1] = *reinterpret_cast<const u32x4*>(wsrc[j] + (cc) * BK + 16);            \
     }                                                                                        \
   } while (0)
-#define DSMOE_ALOAD(cc)                                                                      \
+#define DSMOE_ALOAD(cc, set)                                                                 \
   do {                                                                                       \
-    _Pragma("unroll") for (int i = 0; i < C::A_PER; ++i) ra[i] =                             \
+    _Pragma("unroll") for (int i = 0; i < C::A_PER; ++i) ra[set][i] =                        \
         *reinterpret_cast<const u32x4*>(asrc[i] + (cc) * BK);                                \
-    rsa = sasrc[(cc)];                                                                       \
+    rsa[set] = sasrc[(cc)];                                                                  \
   } while (0)
-#define DSMOE_ASTORE(bb)                                                                     \
+#define DSMOE_ASTORE(bb, set, cc)                                                            \
   do {                                                                                       \
     _Pragma("unroll") for (int i = 0; i < C::A_PER; ++i) if (aval[i])                       \
-        *reinterpret_cast<u32x4*>(&s_a[(bb) * BM * BK + adst[i]]) = ra[i];                   \
-    if (tid < BM) s_sa[(bb) * BM + tid] = rsa;                                               \
+        *reinterpret_cast<u32x4*>(&s_a[(bb) * BM * BK + adst[i]]) = ra[set][i];              \
+    if (tid < BM) {                                                                          \
+      s_scl[((bb) * 2 + 0) * BM + tid] = rsa[set] * s_sw[0][(cc)];                           \
+      s_scl[((bb) * 2 + 1) * BM + tid] = rsa[set] * s_sw[1][(cc)];                           \
+    }                                                                                        \
   } while (0)
 
   f32x4 acc[NI][2];
@@ -645,62 +668,78 @@ __global__ __launch_bounds__(512) void gemm_ws_kernel(GemmProblem p, int64_t n_t
   const int frow = lane & 15;
   const int fseg = (lane >> 4) * 2;
 
-  // prologue: W chunks 0 .. D-1 in flight, A chunk 0 staged
+  // prologue: A chunks 0 .. AS-1 and W chunks 0 .. D-1 in flight; A chunk 0
+  // staged (the weight-block scales were staged above)
+  DSMOE_ALOAD(0, 0);
+  DSMOE_WLOAD(0, 0);
+  if constexpr (AS == 2) DSMOE_ALOAD(min<int64_t>(1, kchunks - 1), 1);
 #pragma unroll
-  for (int d = 0; d < C::D; ++d) DSMOE_WLOAD(min<int64_t>(d, kchunks - 1), d);
-  DSMOE_ALOAD(0);
-  DSMOE_ASTORE(0);
+  for (int d = 1; d < C::D; ++d) DSMOE_WLOAD(min<int64_t>(d, kchunks - 1), d);
+  __syncthreads();
+  DSMOE_ASTORE(0, 0, 0);
   __syncthreads();
 
+  static_assert(SLOTS % AS == 0, "A register sets follow the chunk index");
   for (int64_t c0 = 0; c0 < kchunks; c0 += SLOTS) {
 #pragma unroll
     for (int u = 0; u < SLOTS; ++u) {
       const int64_t c = c0 + u;
+      const int64_t cn = min<int64_t>(c + 1, kchunks - 1);
       // loads are issued unconditionally (clamped to the last chunk) so every
-      // register set is written on every path
-      DSMOE_ALOAD(min<int64_t>(c + 1, kchunks - 1));
+      // register set is written on every path; set u % AS held A(c), which
+      // is in LDS already
+      DSMOE_ALOAD(min<int64_t>(c + AS, kchunks - 1), u % AS);
       DSMOE_WLOAD(min<int64_t>(c + C::D, kchunks - 1), (u + C::D) % SLOTS);
       if (c < kchunks) {
         const int buf = static_cast<int>(c & 1);
-        const float sw = s_sw[my_half][c];
+        const float* scl = s_scl + (buf * 2 + my_half) * BM + (lane >> 4) * 4;
         const i32x8 b0 = cat8(wr[u][0][0], wr[u][0][1]);
         const i32x8 b1 = cat8(wr[u][1][0], wr[u][1][1]);
-        // software pipeline over the row tiles: the MFMAs of tile i are in
-        // flight while tile i-1 is promoted; the scheduling barriers keep the
-        // compiler from hoisting every tile's operands at once (register
-        // pressure)
-        f32x4 pp0 = {0.f, 0.f, 0.f, 0.f}, pp1 = {0.f, 0.f, 0.f, 0.f}, psa = {0.f, 0.f, 0.f, 0.f};
+        // Software pipeline over the row tiles: the LDS operands of tile i+1
+        // are requested before the MFMAs of tile i are issued, and tile i-1
+        // is promoted after them.  Operands, partial sums and scales rotate
+        // through register sets indexed by the (unrolled) tile number, so no
+        // copies are needed; the scheduling barriers keep the compiler from
+        // hoisting every tile's operands at once (register pressure).
+        i32x8 fa[2];
+        f32x4 pr[2][2], ps[3];
+#define DSMOE_FRAG(ii)                                                                          \
+  do {                                                                                          \
+    const int r_ = (ii) * 16 + frow;                                                            \
+    fa[(ii) & 1] = cat8(*reinterpret_cast<const u32x4*>(&s_a[buf * BM * BK + swz(r_, fseg)]),   \
+                        *reinterpret_cast<const u32x4*>(&s_a[buf * BM * BK + swz(r_, fseg + 1)])); \
+    ps[(ii) % 3] = *reinterpret_cast<const f32x4*>(scl + (ii) * 16);                           \
+  } while (0)
+        DSMOE_FRAG(0);
 #pragma unroll
         for (int i = 0; i <= NI; ++i) {
-          f32x4 p0, p1, sa4;
+          if (i + 1 < NI) DSMOE_FRAG(i + 1);
           if (i < NI) {
-            const int r = i * 16 + frow;
-            const i32x8 af = cat8(*reinterpret_cast<const u32x4*>(&s_a[buf * BM * BK + swz(r, fseg)]),
-                                  *reinterpret_cast<const u32x4*>(&s_a[buf * BM * BK + swz(r, fseg + 1)]));
-            sa4 = *reinterpret_cast<const f32x4*>(&s_sa[buf * BM + i * 16 + (lane >> 4) * 4]);
-            p0 = mfma_chunk(af, b0);
-            p1 = mfma_chunk(af, b1);
+            pr[i & 1][0] = mfma_chunk(fa[i & 1], b0);
+            pr[i & 1][1] = mfma_chunk(fa[i & 1], b1);
           }
           if (i > 0) {
+            const int q = (i - 1) & 1, qs = (i - 1) % 3;
 #pragma unroll
             for (int r2 = 0; r2 < 4; ++r2) {
-              const float scl = psa[r2] * sw;
-              acc[i - 1][0][r2] = __builtin_fmaf(pp0[r2], scl, acc[i - 1][0][r2]);
-              acc[i - 1][1][r2] = __builtin_fmaf(pp1[r2], scl, acc[i - 1][1][r2]);
+              acc[i - 1][0][r2] = __builtin_fmaf(pr[q][0][r2], ps[qs][r2], acc[i - 1][0][r2]);
+              acc[i - 1][1][r2] = __builtin_fmaf(pr[q][1][r2], ps[qs][r2], acc[i - 1][1][r2]);
             }
             // pin the promotion here (otherwise it is sunk to the loop end and
             // every tile's partial sums stay live at once)
             asm volatile("" : "+v"(acc[i - 1][0]), "+v"(acc[i - 1][1]));
           }
-          if (i < NI) {
-            pp0 = p0;
-            pp1 = p1;
-            psa = sa4;
-          }
+          // issue order inside the step: the MFMAs of tile i (operands read
+          // one step earlier), the LDS reads of tile i+1, then the promotion
+          // of tile i-1 (its MFMAs were issued one step earlier)
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
           __builtin_amdgcn_sched_barrier(0);
         }
+#undef DSMOE_FRAG
       }
-      DSMOE_ASTORE(static_cast<int>((c + 1) & 1));
+      DSMOE_ASTORE(static_cast<int>((c + 1) & 1), (u + 1) % AS, cn);
       __syncthreads();
     }
   }
@@ -746,8 +785,9 @@ hipError_t launch_ws_bm(const GemmProblem& p, int bm, hipStream_t s) {
     case 16: return launch_ws<16, EPI>(p, s);
     case 32: return launch_ws<32, EPI>(p, s);
     case 64: return launch_ws<64, EPI>(p, s);
+    case 96: return launch_ws<96, EPI>(p, s);
     case 128: return launch_ws<128, EPI>(p, s);
-    default: return launch_ws<192, EPI>(p, s);
+    default: return launch_ws<160, EPI>(p, s);
   }
 }
 
@@ -794,13 +834,15 @@ hipError_t launch_combine(const void* o, const int32_t* inv, int64_t T, int32_t 
 }
 
 // Row-tile height of the weight-streaming kernel for groups of about
-// `rows` rows (0: use the 128-row LDS kernel).  A tile that holds a whole
-// group keeps every weight byte to a single HBM read; the mean group size
-// is padded by half to cover its spread.  Taller groups go to the LDS
-// kernel, whose 128 x BN tiles reuse each staged weight chunk over more rows.
+// `rows_hint` rows (0: use the 128-row LDS kernel).  Every tile multiplies all
+// of its rows, so the height is the mean group size plus a quarter (room for
+// the spread; a group past it takes a second tile).  A tile that holds a
+// whole group keeps every weight byte to a single HBM read.  Taller groups
+// go to the LDS kernel, whose 128 x BN tiles reuse each staged weight chunk
+// over more rows.
 int ws_tile_rows(int64_t rows_hint) {
-  const int64_t want = rows_hint + rows_hint / 2;
-  for (int bm : {16, 32, 64, 128, 192})
+  const int64_t want = rows_hint + rows_hint / 4;
+  for (int bm : {16, 32, 64, 96, 128, 160})
     if (want <= bm) return bm;
   return 0;
 }
