@@ -248,69 +248,83 @@ __device__ __forceinline__ void epi_combine(const GemmProblem& p, const f32x4 (&
 }
 
 // SwiGLU + 1x128 requantisation.  The block tile holds 128 gate columns and
-// the matching 128 up columns; a gate wave owns gate columns
-// [gcol, gcol + 16*NJ) and one up wave owns the same up columns.  Up waves
-// hand their accumulators over through LDS; gate waves form
-// a = silu(g) * u in float32, the row amax over the 128 columns (across the
-// gate waves), the scale and the E4M3 codes; the codes are then stored with
-// 16-byte writes.  s_up: [ROWS][128] f32, s_rmax: [GATE_WAVES][ROWS] f32,
-// s_code: [ROWS][128] bytes.
-template <int NI, int NJ, int ROWS, int GATE_WAVES>
+// the matching 128 up columns.  Waves come in pairs: a gate wave holding gate
+// columns [gcol, gcol + 16*NJ) of some rows and an up wave holding the same up
+// columns of the same rows, with the same lane -> (row, column) map.  Each
+// wave of a pair finishes half of those columns: the gate wave the first
+// NJ/2 16-column slices, the up wave the rest; they swap the other half
+// through LDS, indexed by (slice, lane) so that every access is a contiguous
+// 16-byte-per-lane run.  a = silu(g) * u in float32; a row's amax over its
+// 128 columns is reduced in registers (16 lanes) and across the NSLOTS waves
+// that share the row through s_rmax; then scale = amax / 448 and the E4M3
+// codes, which are stored with 16-byte writes.
+//   s_ex:   [pairs][2][NI][NJ/2][64 lanes] f32x4
+//   s_rmax: [NSLOTS][ROWS] f32
+//   s_code: [ROWS][128] bytes
+template <int NI, int NJ, int ROWS, int NSLOTS>
 __device__ __forceinline__ void epi_swiglu(const GemmProblem& p, const f32x4 (&acc)[NI][NJ],
                                            int64_t row0, int64_t row1, int row_base,
-                                           bool is_gate, int gate_idx, int gcol, int64_t nt,
-                                           float* s_up, float* s_rmax, uint8_t* s_code) {
+                                           bool is_gate, int pair, int slot, int gcol, int64_t nt,
+                                           f32x4* s_ex, float* s_rmax, uint8_t* s_code) {
+  constexpr int HJ = NJ / 2;
+  static_assert(NJ % 2 == 0, "column slices split between the two waves of a pair");
   const int lane = threadIdx.x & 63;
   const int frow = lane & 15;
-  if (!is_gate) {
+  f32x4* ex_gate = s_ex + ((pair * 2 + 0) * NI * HJ) * 64;   // gate values for the up wave
+  f32x4* ex_up = s_ex + ((pair * 2 + 1) * NI * HJ) * 64;     // up values for the gate wave
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          s_up[(row_base + i * 16 + (lane >> 4) * 4 + r) * 128 + gcol + j * 16 + frow] = acc[i][j][r];
-  }
+    for (int j = 0; j < HJ; ++j) {
+      if (is_gate)
+        ex_gate[(i * HJ + j) * 64 + lane] = acc[i][HJ + j];
+      else
+        ex_up[(i * HJ + j) * 64 + lane] = acc[i][j];
+    }
   __syncthreads();
-  float av[NI][NJ][4];
-  if (is_gate) {
+  float av[NI][HJ][4];
+  const int jo = is_gate ? 0 : HJ;
+  const f32x4* ex_other = is_gate ? ex_up : ex_gate;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+  for (int i = 0; i < NI; ++i) {
+#pragma unroll
+    for (int j = 0; j < HJ; ++j) {
+      const f32x4 other = ex_other[(i * HJ + j) * 64 + lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int lr = row_base + i * 16 + (lane >> 4) * 4 + r;
-        float m = 0.f;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const float gt = acc[i][j][r];
-          const float up = s_up[lr * 128 + gcol + j * 16 + frow];
-          const float a = gt / (1.0f + expf(-gt)) * up;
-          av[i][j][r] = a;
-          m = fmaxf(m, fabsf(a));
-        }
-        m = wave_max_width(m, 16);
-        if (frow == 0) s_rmax[gate_idx * ROWS + lr] = m;
+        // scalar selects keep every acc index a constant
+        const float gt = is_gate ? acc[i][j][r] : other[r];
+        const float up = is_gate ? other[r] : acc[i][HJ + j][r];
+        av[i][j][r] = gt / (1.0f + expf(-gt)) * up;
       }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float m = 0.f;
+#pragma unroll
+      for (int j = 0; j < HJ; ++j) m = fmaxf(m, fabsf(av[i][j][r]));
+      m = wave_max_width(m, 16);
+      if (frow == 0) s_rmax[slot * ROWS + row_base + i * 16 + (lane >> 4) * 4 + r] = m;
+    }
   }
   __syncthreads();
   const int64_t I = p.N / 2;
-  if (is_gate) {
+  const int ccol = gcol + jo * 16 + frow;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int lr = row_base + i * 16 + (lane >> 4) * 4 + r;
-        float amax = s_rmax[lr];
+    for (int r = 0; r < 4; ++r) {
+      const int lr = row_base + i * 16 + (lane >> 4) * 4 + r;
+      float amax = s_rmax[lr];
 #pragma unroll
-        for (int w = 1; w < GATE_WAVES; ++w) amax = fmaxf(amax, s_rmax[w * ROWS + lr]);
-        const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+      for (int w = 1; w < NSLOTS; ++w) amax = fmaxf(amax, s_rmax[w * ROWS + lr]);
+      const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          s_code[lr * 128 + gcol + j * 16 + frow] = static_cast<uint8_t>(e4m3_encode(av[i][j][r] / s));
-        const int64_t row = row0 + lr;
-        if (gate_idx == 0 && frow == 0 && row < row1) p.c_scale[row * (I / BK) + nt] = s;
-      }
-  }
+      for (int j = 0; j < HJ; ++j)
+        s_code[lr * 128 + ccol + j * 16] = static_cast<uint8_t>(e4m3_encode(av[i][j][r] / s));
+      const int64_t row = row0 + lr;
+      if (slot == 0 && frow == 0 && row < row1) p.c_scale[row * (I / BK) + nt] = s;
+    }
   __syncthreads();
   for (int idx = threadIdx.x; idx < ROWS * 8; idx += blockDim.x) {
     const int lr = idx >> 3, seg = idx & 7;
@@ -523,9 +537,9 @@ __global__ __launch_bounds__(2 * BN) void gemm_lds_kernel(GemmProblem p, int64_t
     epi_combine<4, 4>(p, acc, row0, row1, wm * 64, nt * BN + wn * 64,
                       reinterpret_cast<float*>(&s_a[0][0]) + wave * 16 * 64);
   } else {  // waves with wn 0,1 hold gate columns, 2,3 the matching up columns
-    epi_swiglu<4, 4, LBM, 2>(p, acc, row0, row1, wm * 64, wn < 2, wn & 1, (wn & 1) * 64, nt,
-                             reinterpret_cast<float*>(&s_b[0][0]),
-                             reinterpret_cast<float*>(&s_sa[0][0]), &s_a[1][0]);
+    epi_swiglu<4, 4, LBM, 4>(p, acc, row0, row1, wm * 64, wn < 2, wm * 2 + (wn & 1), wn, (wn & 1) * 64,
+                             nt, reinterpret_cast<f32x4*>(&s_b[0][0]),
+                             reinterpret_cast<float*>(&s_a[0][0]), &s_a[1][0]);
   }
 }
 
@@ -548,9 +562,9 @@ struct WsCfg {
   static constexpr int A_SEGS = BM * 8;          // 16-byte segments of one A chunk
   static constexpr int A_PER = (A_SEGS + THREADS - 1) / THREADS;
   // LDS: two A stages + the two halves' row scales during the K loop; the
-  // SwiGLU epilogue reuses it for the up half (f32), the row maxima and the codes
+  // SwiGLU epilogue reuses it for the gate/up exchange (f32), the row maxima and the codes
   static constexpr int MAIN_BYTES = 2 * BM * BK + 2 * 2 * BM * 4;
-  static constexpr int EPI_BYTES = BM * 128 * 4 + 4 * BM * 4 + BM * 128;
+  static constexpr int EPI_BYTES = BM * 128 * 4 + 8 * BM * 4 + BM * 128;
   static constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
 };
 
@@ -752,11 +766,11 @@ __global__ __launch_bounds__(512) void gemm_ws_kernel(GemmProblem p, int64_t n_t
   } else if constexpr (EPI == Epilogue::kCombine) {
     epi_combine<NI, 2>(p, acc, row0, row1, 0, nt * C::BN + wave * 32,
                        reinterpret_cast<float*>(s_raw) + wave * 16 * 32);
-  } else {  // waves 0-3 hold gate columns 32w.., waves 4-7 the matching up columns
-    epi_swiglu<NI, 2, BM, 4>(p, acc, row0, row1, 0, wave < 4, wave & 3, (wave & 3) * 32, nt,
-                             reinterpret_cast<float*>(s_raw),
+  } else {  // waves 0-3 hold gate columns 32w.., waves 4-7 the matching up columns (pairs w, w+4)
+    epi_swiglu<NI, 2, BM, 8>(p, acc, row0, row1, 0, wave < 4, wave & 3, wave, (wave & 3) * 32, nt,
+                             reinterpret_cast<f32x4*>(s_raw),
                              reinterpret_cast<float*>(s_raw + BM * 128 * 4),
-                             s_raw + BM * 128 * 4 + 4 * BM * 4);
+                             s_raw + BM * 128 * 4 + 8 * BM * 4);
   }
 }
 
