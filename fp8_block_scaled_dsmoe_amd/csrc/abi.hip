@@ -53,7 +53,8 @@ dsmoe_status check_routing_shape(int64_t T, int32_t E, int32_t G, int32_t Mg, in
 
 // Workspace layout of dsmoe_moe_forward (every region 256-byte aligned).
 struct Layout {
-  size_t qx, sx, logits, topk, gates, offsets, offsets_ext, perm, inv, row_gate, qa, sa, o, total;
+  size_t qx, sx, logits, router_part, topk, gates, offsets, offsets_ext, perm, inv, row_gate, qa, sa, o,
+      total;
 };
 
 Layout layout_for(const dsmoe_moe_desc& d, int64_t T) {
@@ -69,6 +70,7 @@ Layout layout_for(const dsmoe_moe_desc& d, int64_t T) {
   L.qx = take(static_cast<size_t>(T) * d.H);
   L.sx = take(static_cast<size_t>(T) * (d.H / 128) * 4);
   L.logits = take(static_cast<size_t>(T) * d.E * 4);
+  L.router_part = take(dsmoe::router_partial_bytes(T, d.H, d.E));
   L.topk = take(TK * 4);
   L.gates = take(TK * 4);
   L.offsets = take((static_cast<size_t>(d.E) + 1) * 4);
@@ -275,7 +277,7 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
   // router logits (bf16 MFMA, FP32 accumulation)
   DSMOE_TRY(dsmoe::launch_router_logits(static_cast<const uint16_t*>(x),
                                         static_cast<const uint16_t*>(w->router_w), T, H, E,
-                                        logits, st));
+                                        logits, reinterpret_cast<float*>(ws + L.router_part), st));
   DSMOE_MARK(2);
   // group-limited top-K routing
   DSMOE_TRY(dsmoe::launch_route_select(logits, bias, T, E, d->G, d->Mg, K, topk, gates,

@@ -15,8 +15,12 @@ hipError_t launch_quant_w(const void* w, bool w_f32, int64_t n_mats, int64_t n, 
                           uint8_t* q, float* scale, hipStream_t s);
 
 // route.hip
+// H is split over router_splits() blocks for small T; the splits' partial
+// sums go to `partial` (router_partial_bytes(), NULL when that is 0)
+int router_splits(int64_t T, int64_t H, int32_t E);
+size_t router_partial_bytes(int64_t T, int64_t H, int32_t E);
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, int64_t T, int64_t H,
-                                int32_t E, float* logits, hipStream_t s);
+                                int32_t E, float* logits, float* partial, hipStream_t s);
 // topk/gates + per-expert counts (counts are zeroed first by the launcher)
 hipError_t launch_route_select(const float* logits, const float* bias, int64_t T, int32_t E,
                                int32_t G, int32_t Mg, int32_t K, int32_t* topk_idx,

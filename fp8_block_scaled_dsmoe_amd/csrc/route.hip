@@ -29,20 +29,30 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // Router logits z[T][E] = x[T][H] . Wr[E][H]^T on bf16 MFMA (16x16x32).
 // Block tile 64 tokens x 64 experts, K step 64, LDS double buffer with a
 // 16-byte-segment XOR swizzle; four waves, each 32 x 32 (2 x 2 MFMA tiles).
+// Small batches split H over blockIdx.z (router_splits): each split writes
+// its partial sums, and a second kernel adds the splits in a fixed order, so
+// the result does not depend on scheduling.
 // ---------------------------------------------------------------------------
 constexpr int RT = 64, RE = 64, RK = 64;  // RK bf16 = 128 bytes per row
 
-__device__ __forceinline__ int swz(int row, int seg) { return row * 128 + ((seg ^ (row & 7)) << 4); }
+// 16-byte segment seg of row `row` sits in slot seg ^ key(row); the key is
+// distinct over any 8 consecutive rows and over the even (odd) rows of 16, so
+// a 16-lane read of 16 rows spreads over all LDS banks.
+__device__ __forceinline__ int swz(int row, int seg) {
+  return row * 128 + ((seg ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+}
 
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ wr,
                                                             int64_t T, int64_t H, int32_t E,
-                                                            float* __restrict__ z) {
+                                                            int64_t k_len, float* __restrict__ z) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][RT * 128];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RT;
   const int e0 = blockIdx.y * RE;
+  const int64_t k_begin = static_cast<int64_t>(blockIdx.z) * k_len;   // this split's columns
+  z += static_cast<int64_t>(blockIdx.z) * T * E;
 
   // global -> register loads: 2 x 16 bytes of x and of Wr per thread per step
   const uint16_t* xsrc[2];
@@ -55,8 +65,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
     lseg[i] = idx & 7;
     const int64_t tr = min<int64_t>(t0 + lrow[i], T - 1);
     const int er = min(e0 + lrow[i], E - 1);
-    xsrc[i] = x + tr * H + lseg[i] * 8;
-    wsrc[i] = wr + static_cast<int64_t>(er) * H + lseg[i] * 8;
+    xsrc[i] = x + tr * H + k_begin + lseg[i] * 8;
+    wsrc[i] = wr + static_cast<int64_t>(er) * H + k_begin + lseg[i] * 8;
   }
   u32x4 xr[2], wrr[2];
 #define DSMOE_GLOAD(k0)                                                    \
@@ -81,7 +91,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t steps = H / RK;
+  const int64_t steps = k_len / RK;
   DSMOE_GLOAD(0);
   DSMOE_SSTORE(0);
   __syncthreads();
@@ -120,6 +130,22 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
         if (t < T && e < E) z[t * E + e] = acc[i][j][r];
       }
     }
+}
+
+// z[t][e] = sum over splits s = 0, 1, ... of part[s][t][e], in that order;
+// 4 values per thread.
+__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part,
+                                                            int32_t splits, int64_t n,
+                                                            float* __restrict__ z) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 v = *reinterpret_cast<const f32x4*>(part + i);
+  for (int32_t sp = 1; sp < splits; ++sp) {
+    const f32x4 u = *reinterpret_cast<const f32x4*>(part + static_cast<int64_t>(sp) * n + i);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = v[r] + u[r];
+  }
+  *reinterpret_cast<f32x4*>(z + i) = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -342,11 +368,35 @@ __global__ void update_bias_kernel(float* __restrict__ bias, const int32_t* __re
 
 }  // namespace
 
+int router_splits(int64_t T, int64_t H, int32_t E) {
+  // enough blocks to cover the device (about 512), each split at least 256
+  // columns long, and T * E a multiple of 4 for the reduction
+  const int64_t base = ((T + RT - 1) / RT) * ((E + RE - 1) / RE);
+  if (base <= 0 || base >= 512 || (T * E) % 4 != 0) return 1;
+  int64_t want = (512 + base - 1) / base;
+  const int64_t steps = H / RK;
+  int best = 1;
+  for (int64_t sp = 2; sp <= want && sp * 4 <= steps; ++sp)
+    if (steps % sp == 0) best = static_cast<int>(sp);
+  return best;
+}
+
+size_t router_partial_bytes(int64_t T, int64_t H, int32_t E) {
+  const int sp = router_splits(T, H, E);
+  return sp > 1 ? static_cast<size_t>(sp) * T * E * sizeof(float) : 0;
+}
+
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, int64_t T, int64_t H,
-                                int32_t E, float* logits, hipStream_t s) {
+                                int32_t E, float* logits, float* partial, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((T + RT - 1) / RT), static_cast<unsigned>((E + RE - 1) / RE));
-  router_logits_kernel<<<grid, 256, 0, s>>>(x, wr, T, H, E, logits);
+  const int sp = router_splits(T, H, E);
+  const dim3 grid(static_cast<unsigned>((T + RT - 1) / RT), static_cast<unsigned>((E + RE - 1) / RE),
+                  static_cast<unsigned>(sp));
+  router_logits_kernel<<<grid, 256, 0, s>>>(x, wr, T, H, E, H / sp, sp > 1 ? partial : logits);
+  if (sp > 1) {
+    const int64_t n = T * E;
+    router_reduce_kernel<<<static_cast<unsigned>((n / 4 + 255) / 256), 256, 0, s>>>(partial, sp, n, logits);
+  }
   return hipGetLastError();
 }
 
