@@ -143,46 +143,21 @@ inline int64_t pad_grid(int64_t blocks) {
 // (i, j, r) holds local row row_base + 16i + 4*(lane/16) + r and column
 // col0 + 16j + lane%16 of the output; row0 is the tile's first output row.
 // ---------------------------------------------------------------------------
+// Row-wise stores.  Each 16-row slice of the wave tile goes through the
+// wave's own LDS scratch so that a lane then owns a run of 4*NJ contiguous
+// columns of one row and writes it with 16-byte stores:
+//   kStore      c[row][col] = acc
+//   kGateStore  c[row][col] = acc * row_gate[row]
+//   kCombine    y[t][col] = acc + sum over k (ascending) of o[inv[t][k]][col],
+//               t = row - row_base, read with 16/32-byte loads
 template <int NI, int NJ, Epilogue EPI>
-__device__ __forceinline__ void epi_store(const GemmProblem& p, const f32x4 (&acc)[NI][NJ],
-                                          int64_t row0, int64_t row1, int row_base,
-                                          int64_t col0) {
-  const int lane = threadIdx.x & 63;
-  const int64_t N = p.N;
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = row0 + row_base + i * 16 + (lane >> 4) * 4 + r;
-      if (row >= row1) continue;
-      float gsc = 1.0f;
-      if constexpr (EPI == Epilogue::kGateStore) gsc = p.row_gate[row];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int64_t col = col0 + j * 16 + (lane & 15);
-        float v = acc[i][j][r];
-        if constexpr (EPI == Epilogue::kGateStore) v = v * gsc;
-        if (p.c_f32)
-          static_cast<float*>(p.c)[row * N + col] = v;
-        else
-          static_cast<uint16_t*>(p.c)[row * N + col] = f32_to_bf16(v);
-      }
-    }
-}
-
-// y[t][col] = acc + sum over k (ascending) of o[inv[t][k]][col].  Each
-// 16-row slice of the wave tile goes through the wave's own LDS scratch so
-// that a lane then owns a run of 4*NJ contiguous columns of one row and reads
-// the routed rows with 16/32-byte loads.
-template <int NI, int NJ>
-__device__ __forceinline__ void epi_combine(const GemmProblem& p, const f32x4 (&acc)[NI][NJ],
-                                            int64_t row0, int64_t row1, int row_base,
-                                            int64_t col0, float* scratch) {
+__device__ __forceinline__ void epi_rows(const GemmProblem& p, const f32x4 (&acc)[NI][NJ],
+                                         int64_t row0, int64_t row1, int row_base, int64_t col0,
+                                         float* scratch) {
   constexpr int NCOL = 16 * NJ;
   constexpr int PER = NCOL / 4;  // columns per lane
   const int lane = threadIdx.x & 63;
   const int64_t N = p.N;
-  const int32_t K_ = p.topk;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
 #pragma unroll
@@ -201,38 +176,47 @@ __device__ __forceinline__ void epi_combine(const GemmProblem& p, const f32x4 (&
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_wave_barrier();
     if (row < row1) {
-      const int64_t tok = row - p.row_base;
-      const int32_t* inv_t = p.inv + tok * K_;
       const int64_t col = col0 + lc;
-      for (int k = 0; k < K_; ++k) {
-        const int64_t orow = inv_t[k];
-        if (p.c_f32) {
-          const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.o_routed) + orow * N + col);
+      int64_t orow = row;
+      if constexpr (EPI == Epilogue::kGateStore) {
+        const float gsc = p.row_gate[row];
 #pragma unroll
-          for (int q = 0; q < PER / 4; ++q) {
-            const f32x4 o4 = src[q];
+        for (int e = 0; e < PER; ++e) v[e] = v[e] * gsc;
+      }
+      if constexpr (EPI == Epilogue::kCombine) {
+        orow = row - p.row_base;   // the token
+        const int32_t K_ = p.topk;
+        const int32_t* inv_t = p.inv + orow * K_;
+        for (int k = 0; k < K_; ++k) {
+          const int64_t src = inv_t[k];
+          if (p.c_f32) {
+            const f32x4* o4p = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.o_routed) + src * N + col);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[4 * q + e] = v[4 * q + e] + o4[e];
-          }
-        } else {
-          const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.o_routed) + orow * N + col);
+            for (int q = 0; q < PER / 4; ++q) {
+              const f32x4 o4 = o4p[q];
 #pragma unroll
-          for (int q = 0; q < PER / 8; ++q) {
-            const u32x4 o8 = src[q];
+              for (int e = 0; e < 4; ++e) v[4 * q + e] = v[4 * q + e] + o4[e];
+            }
+          } else {
+            const u32x4* o8p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.o_routed) + src * N + col);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              v[8 * q + 2 * e] = v[8 * q + 2 * e] + __uint_as_float(o8[e] << 16);
-              v[8 * q + 2 * e + 1] = v[8 * q + 2 * e + 1] + __uint_as_float(o8[e] & 0xFFFF0000u);
+            for (int q = 0; q < PER / 8; ++q) {
+              const u32x4 o8 = o8p[q];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                v[8 * q + 2 * e] = v[8 * q + 2 * e] + __uint_as_float(o8[e] << 16);
+                v[8 * q + 2 * e + 1] = v[8 * q + 2 * e + 1] + __uint_as_float(o8[e] & 0xFFFF0000u);
+              }
             }
           }
         }
       }
       if (p.c_f32) {
-        f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(p.c) + tok * N + col);
+        f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(p.c) + orow * N + col);
 #pragma unroll
         for (int q = 0; q < PER / 4; ++q) dst[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
       } else {
-        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.c) + tok * N + col);
+        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.c) + orow * N + col);
 #pragma unroll
         for (int q = 0; q < PER / 8; ++q) {
           u32x4 w;
@@ -499,43 +483,60 @@ __global__ __launch_bounds__(2 * BN) void gemm_lds_kernel(GemmProblem p, int64_t
     if (c + S - 1 < kchunks) DSMOE_ISSUE(c + S - 1, static_cast<int>((c + S - 1) % S));
     const float sw = s_sw[my_half][c];
 
-    i32x8 af[4], bfr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 64 + i * 16 + frow;
-      af[i] = cat8(*reinterpret_cast<const u32x4*>(&s_a[buf][swz(r, fseg)]),
-                   *reinterpret_cast<const u32x4*>(&s_a[buf][swz(r, fseg + 1)]));
-    }
+    // The chunk's 4 x 4 MFMA tiles run row by row: the W fragments and the
+    // first A fragment are read first, then each row step issues its 4 MFMAs,
+    // reads the next row's A fragment and scales, and promotes the previous
+    // row, so LDS reads, MFMAs and promotions overlap; the scheduling-group
+    // barriers fix that order.  Partial sums alternate between two register
+    // sets by row parity (no copies).
+    i32x8 bfr[4], fa[2];
+    f32x4 sa4[2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = wn * 64 + j * 16 + frow;
       bfr[j] = cat8(*reinterpret_cast<const u32x4*>(&s_b[buf][swz(r, fseg)]),
                     *reinterpret_cast<const u32x4*>(&s_b[buf][swz(r, fseg + 1)]));
     }
-    float scl[4][4];
+#define DSMOE_AFRAG(ii)                                                                       \
+  do {                                                                                        \
+    const int r_ = wm * 64 + (ii) * 16 + frow;                                                \
+    fa[(ii) & 1] = cat8(*reinterpret_cast<const u32x4*>(&s_a[buf][swz(r_, fseg)]),            \
+                        *reinterpret_cast<const u32x4*>(&s_a[buf][swz(r_, fseg + 1)]));       \
+    sa4[(ii) & 1] = *reinterpret_cast<const f32x4*>(&s_sa[buf][wm * 64 + (ii) * 16 + (lane >> 4) * 4]); \
+  } while (0)
+    DSMOE_AFRAG(0);
+    f32x4 part[2][4];
+    float scl[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 sa4 = *reinterpret_cast<const f32x4*>(&s_sa[buf][wm * 64 + i * 16 + (lane >> 4) * 4]);
+    for (int i = 0; i <= 4; ++i) {
+      if (i < 4) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) scl[i][r] = sa4[r] * sw;
-    }
+        for (int j = 0; j < 4; ++j) part[i & 1][j] = mfma_chunk(fa[i & 1], bfr[j]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 part = mfma_chunk(af[i], bfr[j]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(part[r], scl[i][r], acc[i][j][r]);
+        for (int r = 0; r < 4; ++r) scl[i & 1][r] = sa4[i & 1][r] * sw;
       }
+      if (i + 1 < 4) DSMOE_AFRAG(i + 1);
+      if (i > 0) {
+        const int q = (i - 1) & 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[i - 1][j][r] = __builtin_fmaf(part[q][j][r], scl[q][r], acc[i - 1][j][r]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);    // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);   // VALU
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#undef DSMOE_AFRAG
   }
 #undef DSMOE_ISSUE
   __syncthreads();  // all waves are done with the staging buffers (epilogues reuse them)
 
-  if constexpr (EPI == Epilogue::kStore || EPI == Epilogue::kGateStore) {
-    epi_store<4, 4, EPI>(p, acc, row0, row1, wm * 64, nt * BN + wn * 64);
-  } else if constexpr (EPI == Epilogue::kCombine) {
-    epi_combine<4, 4>(p, acc, row0, row1, wm * 64, nt * BN + wn * 64,
-                      reinterpret_cast<float*>(&s_a[0][0]) + wave * 16 * 64);
+  if constexpr (EPI != Epilogue::kSwiGLUQuant) {
+    epi_rows<4, 4, EPI>(p, acc, row0, row1, wm * 64, nt * BN + wn * 64,
+                        reinterpret_cast<float*>(&s_a[0][0]) + wave * 16 * 64);
   } else {  // waves with wn 0,1 hold gate columns, 2,3 the matching up columns
     epi_swiglu<4, 4, LBM, 4>(p, acc, row0, row1, wm * 64, wn < 2, wm * 2 + (wn & 1), wn, (wn & 1) * 64,
                              nt, reinterpret_cast<f32x4*>(&s_b[0][0]),
@@ -562,10 +563,13 @@ struct WsCfg {
   static constexpr int A_SEGS = BM * 8;          // 16-byte segments of one A chunk
   static constexpr int A_PER = (A_SEGS + THREADS - 1) / THREADS;
   // LDS: two A stages + the two halves' row scales during the K loop; the
-  // SwiGLU epilogue reuses it for the gate/up exchange (f32), the row maxima and the codes
+  // SwiGLU epilogue reuses it for the gate/up exchange (f32), the row maxima
+  // and the codes, the row-wise epilogues for one 16 x 32 f32 slice per wave
   static constexpr int MAIN_BYTES = 2 * BM * BK + 2 * 2 * BM * 4;
   static constexpr int EPI_BYTES = BM * 128 * 4 + 8 * BM * 4 + BM * 128;
-  static constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+  static constexpr int ROWS_BYTES = NW * 16 * 32 * 4;
+  static constexpr int MAX_A = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+  static constexpr int LDS_BYTES = MAX_A > ROWS_BYTES ? MAX_A : ROWS_BYTES;
 };
 
 template <int BM, Epilogue EPI>
@@ -761,11 +765,9 @@ __global__ __launch_bounds__(512) void gemm_ws_kernel(GemmProblem p, int64_t n_t
 #undef DSMOE_ALOAD
 #undef DSMOE_ASTORE
 
-  if constexpr (EPI == Epilogue::kStore || EPI == Epilogue::kGateStore) {
-    epi_store<NI, 2, EPI>(p, acc, row0, row1, 0, nt * C::BN + wave * 32);
-  } else if constexpr (EPI == Epilogue::kCombine) {
-    epi_combine<NI, 2>(p, acc, row0, row1, 0, nt * C::BN + wave * 32,
-                       reinterpret_cast<float*>(s_raw) + wave * 16 * 32);
+  if constexpr (EPI != Epilogue::kSwiGLUQuant) {
+    epi_rows<NI, 2, EPI>(p, acc, row0, row1, 0, nt * C::BN + wave * 32,
+                         reinterpret_cast<float*>(s_raw) + wave * 16 * 32);
   } else {  // waves 0-3 hold gate columns 32w.., waves 4-7 the matching up columns (pairs w, w+4)
     epi_swiglu<NI, 2, BM, 8>(p, acc, row0, row1, 0, wave < 4, wave & 3, wave, (wave & 3) * 32, nt,
                              reinterpret_cast<f32x4*>(s_raw),

@@ -143,6 +143,10 @@ def test_tiny_layer_deterministic():
     LayerConfig("ragged", T=77, H=256, E=8, G=2, Mg=1, K=3, I=128, router_std=0.05, bias_range=0.02),
     LayerConfig("one_expert", T=130, H=384, E=1, G=1, Mg=1, K=1, I=256, router_std=0.05),
     LayerConfig("wide", T=300, H=1024, E=32, G=8, Mg=4, K=8, I=384, router_std=0.02, bias_range=0.01),
+    # few tokens: the shared expert's down-projection with the combine runs on
+    # 16- and 32-row weight-streaming tiles
+    LayerConfig("few7", T=7, H=512, E=16, G=4, Mg=2, K=4, I=256, router_std=0.05),
+    LayerConfig("few20", T=20, H=512, E=16, G=4, Mg=2, K=4, I=256, router_std=0.05),
 ], ids=lambda c: c.name)
 def test_layer_shapes(cfg):
     _layer_case(cfg, torch.float32)
