@@ -58,6 +58,22 @@ __device__ __forceinline__ float wave_max_width(float v, int width) {
   return v;
 }
 
+// Maximum of non-negative values (or NaN) over each aligned group of 16
+// lanes (one DPP row), left in every lane of the group: swap neighbours, swap
+// pairs (quad permutations), then mirror within each 8-lane half and within
+// the row.  For non-negative floats the order of the bit patterns is the
+// order of the values, so an unsigned max does it without canonicalising
+// moves; there is no LDS round trip (a cross-lane shuffle goes through the
+// LDS crossbar).
+__device__ __forceinline__ float row16_max_nonneg(float v) {
+  uint32_t b = __float_as_uint(v);
+  b = max(b, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b), 0xB1, 0xF, 0xF, false)));
+  b = max(b, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b), 0x4E, 0xF, 0xF, false)));
+  b = max(b, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b), 0x141, 0xF, 0xF, false)));
+  b = max(b, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b), 0x140, 0xF, 0xF, false)));
+  return __uint_as_float(b);
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 }  // namespace dsmoe

@@ -238,10 +238,13 @@ __device__ __forceinline__ void epi_rows(const GemmProblem& p, const f32x4 (&acc
 // wave of a pair finishes half of those columns: the gate wave the first
 // NJ/2 16-column slices, the up wave the rest; they swap the other half
 // through LDS, indexed by (slice, lane) so that every access is a contiguous
-// 16-byte-per-lane run.  a = silu(g) * u in float32; a row's amax over its
-// 128 columns is reduced in registers (16 lanes) and across the NSLOTS waves
-// that share the row through s_rmax; then scale = amax / 448 and the E4M3
-// codes, which are stored with 16-byte writes.
+// 16-byte-per-lane run.  a = silu(g) * u in float32, with silu(g) =
+// g * rcp(1 + exp(-g)) (a few ulps, as any float32 evaluation); a row's amax
+// over its 128 columns is reduced in registers (16 lanes, DPP) and across
+// the NSLOTS waves that share the row through s_rmax by one thread per row,
+// which also forms scale = amax / 448 (IEEE division), stores it and leaves
+// 1 / scale for the code pass: code = E4M3(a * (1 / scale)), within an ulp
+// of a / scale.  The codes are stored with 16-byte writes.
 //   s_ex:   [pairs][2][NI][NJ/2][64 lanes] f32x4
 //   s_rmax: [NSLOTS][ROWS] f32
 //   s_code: [ROWS][128] bytes
@@ -279,7 +282,7 @@ __device__ __forceinline__ void epi_swiglu(const GemmProblem& p, const f32x4 (&a
         // scalar selects keep every acc index a constant
         const float gt = is_gate ? acc[i][j][r] : other[r];
         const float up = is_gate ? other[r] : acc[i][HJ + j][r];
-        av[i][j][r] = gt / (1.0f + expf(-gt)) * up;
+        av[i][j][r] = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * up;
       }
     }
 #pragma unroll
@@ -287,27 +290,34 @@ __device__ __forceinline__ void epi_swiglu(const GemmProblem& p, const f32x4 (&a
       float m = 0.f;
 #pragma unroll
       for (int j = 0; j < HJ; ++j) m = fmaxf(m, fabsf(av[i][j][r]));
-      m = wave_max_width(m, 16);
+      m = row16_max_nonneg(m);
       if (frow == 0) s_rmax[slot * ROWS + row_base + i * 16 + (lane >> 4) * 4 + r] = m;
     }
   }
   __syncthreads();
   const int64_t I = p.N / 2;
+  // one thread per row: the row's scale (stored) and its reciprocal, left in
+  // slot 0 of s_rmax (each thread reads and writes only its own row)
+  for (int lr = threadIdx.x; lr < ROWS; lr += blockDim.x) {
+    float amax = s_rmax[lr];
+#pragma unroll
+    for (int w = 1; w < NSLOTS; ++w) amax = fmaxf(amax, s_rmax[w * ROWS + lr]);
+    const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+    s_rmax[lr] = 1.0f / sc;
+    const int64_t row = row0 + lr;
+    if (row < row1) p.c_scale[row * (I / BK) + nt] = sc;
+  }
+  __syncthreads();
   const int ccol = gcol + jo * 16 + frow;
 #pragma unroll
   for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int lr = row_base + i * 16 + (lane >> 4) * 4 + r;
-      float amax = s_rmax[lr];
-#pragma unroll
-      for (int w = 1; w < NSLOTS; ++w) amax = fmaxf(amax, s_rmax[w * ROWS + lr]);
-      const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+      const float rs = s_rmax[lr];
 #pragma unroll
       for (int j = 0; j < HJ; ++j)
-        s_code[lr * 128 + ccol + j * 16] = static_cast<uint8_t>(e4m3_encode(av[i][j][r] / s));
-      const int64_t row = row0 + lr;
-      if (slot == 0 && frow == 0 && row < row1) p.c_scale[row * (I / BK) + nt] = s;
+        s_code[lr * 128 + ccol + j * 16] = static_cast<uint8_t>(e4m3_encode(av[i][j][r] * rs));
     }
   __syncthreads();
   for (int idx = threadIdx.x; idx < ROWS * 8; idx += blockDim.x) {

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = wave_max_width(amax, 16);
+  amax = row16_max_nonneg(amax);
   const float s = scale_from_amax(amax);
   *reinterpret_cast<uint2*>(q + idx) = encode8(v, s);
   if (sub == 0) scale[r * tiles_per_row + j] = s;
