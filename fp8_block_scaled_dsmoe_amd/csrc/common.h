@@ -50,6 +50,17 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
   return sign | ((e << 3) + keep);
 }
 
+// E4M3 codes of two values (low byte: a, next byte: b) with gfx950's packed
+// conversion, which rounds to nearest even like e4m3_encode and gives the same
+// code for every float with |v| <= 464; past that it gives NaN where
+// e4m3_encode saturates, so the values are clamped to +-448 first (the two
+// then agree on every input but NaN).
+__device__ __forceinline__ uint32_t e4m3_encode2(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+}
+
 // ---------------------------------------------------------------------------
 // Wave helpers
 // ---------------------------------------------------------------------------

@@ -244,7 +244,8 @@ __device__ __forceinline__ void epi_rows(const GemmProblem& p, const f32x4 (&acc
 // the NSLOTS waves that share the row through s_rmax by one thread per row,
 // which also forms scale = amax / 448 (IEEE division), stores it and leaves
 // 1 / scale for the code pass: code = E4M3(a * (1 / scale)), within an ulp
-// of a / scale.  The codes are stored with 16-byte writes.
+// of a / scale, by the hardware conversion.  The codes are stored with
+// 16-byte writes.
 //   s_ex:   [pairs][2][NI][NJ/2][64 lanes] f32x4
 //   s_rmax: [NSLOTS][ROWS] f32
 //   s_code: [ROWS][128] bytes
@@ -312,12 +313,15 @@ __device__ __forceinline__ void epi_swiglu(const GemmProblem& p, const f32x4 (&a
 #pragma unroll
   for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 4; r += 2) {   // rows lr, lr + 1: one packed conversion
       const int lr = row_base + i * 16 + (lane >> 4) * 4 + r;
-      const float rs = s_rmax[lr];
+      const float rs0 = s_rmax[lr], rs1 = s_rmax[lr + 1];
 #pragma unroll
-      for (int j = 0; j < HJ; ++j)
-        s_code[lr * 128 + ccol + j * 16] = static_cast<uint8_t>(e4m3_encode(av[i][j][r] * rs));
+      for (int j = 0; j < HJ; ++j) {
+        const uint32_t c2 = e4m3_encode2(av[i][j][r] * rs0, av[i][j][r + 1] * rs1);
+        s_code[lr * 128 + ccol + j * 16] = static_cast<uint8_t>(c2);
+        s_code[(lr + 1) * 128 + ccol + j * 16] = static_cast<uint8_t>(c2 >> 8);
+      }
     }
   __syncthreads();
   for (int idx = threadIdx.x; idx < ROWS * 8; idx += blockDim.x) {
@@ -557,43 +561,53 @@ __global__ __launch_bounds__(2 * BN) void gemm_lds_kernel(GemmProblem p, int64_t
 // ===========================================================================
 // gemm_ws_kernel: weight streaming for groups of few rows
 // ===========================================================================
-template <int BM>
+#ifndef DSMOE_WS_STORE_WAVES
+#define DSMOE_WS_STORE_WAVES 8
+#endif
+constexpr int kWsStoreWaves = DSMOE_WS_STORE_WAVES;
+
+template <int BM, int NW_, bool SWIGLU>
 struct WsCfg {
-  static constexpr int NW = 8;
-  static constexpr int THREADS = 512;
-  static constexpr int BN = 256;                 // 8 waves x 32 columns
+  static constexpr int NW = NW_;                 // waves (8, or 4 for two blocks per CU)
+  static constexpr int THREADS = NW * 64;
+  static constexpr int BN = NW * 32;             // 32 columns per wave
+  static constexpr int HALVES = BN / 128;        // 128-column weight-scale blocks
   static constexpr int NI = BM / 16;             // row tiles per wave
   static constexpr int D = 3;                    // W chunks loaded ahead
   // A chunks are loaded A_SETS ahead.  Two sets keep the wait for the next A
   // chunk from draining the weight stream (see the main loop); small tiles
   // keep one set so that their register count allows four waves per SIMD
   // (two blocks per CU), which doubles their weight bytes in flight instead.
-  static constexpr int A_SETS = BM >= 64 ? 2 : 1;
+  static constexpr int A_SETS = (BM >= 64 && NW == 8) ? 2 : 1;
   static constexpr int SLOTS = D + 1;            // W register sets
   static constexpr int A_SEGS = BM * 8;          // 16-byte segments of one A chunk
   static constexpr int A_PER = (A_SEGS + THREADS - 1) / THREADS;
-  // LDS: two A stages + the two halves' row scales during the K loop; the
-  // SwiGLU epilogue reuses it for the gate/up exchange (f32), the row maxima
-  // and the codes, the row-wise epilogues for one 16 x 32 f32 slice per wave
-  static constexpr int MAIN_BYTES = 2 * BM * BK + 2 * 2 * BM * 4;
-  static constexpr int EPI_BYTES = BM * 128 * 4 + 8 * BM * 4 + BM * 128;
+  // LDS: two A stages + the row scales of each 128-column half during the K
+  // loop; the SwiGLU epilogue reuses it for the gate/up exchange (f32), the
+  // row maxima and the codes, the row-wise epilogues for one 16 x 32 f32
+  // slice per wave
+  static constexpr int MAIN_BYTES = 2 * BM * BK + 2 * HALVES * BM * 4;
+  static constexpr int EPI_BYTES = SWIGLU ? BM * 128 * 4 + 8 * BM * 4 + BM * 128 : 0;
   static constexpr int ROWS_BYTES = NW * 16 * 32 * 4;
   static constexpr int MAX_A = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
   static constexpr int LDS_BYTES = MAX_A > ROWS_BYTES ? MAX_A : ROWS_BYTES;
 };
 
-template <int BM, Epilogue EPI>
-__global__ __launch_bounds__(512) void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
-  using C = WsCfg<BM>;
+template <int BM, int NW, Epilogue EPI>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(8 / NW)))
+void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
+  using C = WsCfg<BM, NW, EPI == Epilogue::kSwiGLUQuant>;
+  static_assert(EPI != Epilogue::kSwiGLUQuant || NW == 8, "SwiGLU tiles hold 128 gate + 128 up columns");
   constexpr int NI = C::NI;
   constexpr int SLOTS = C::SLOTS;
+  constexpr int HV = C::HALVES;
   __shared__ __attribute__((aligned(1024))) uint8_t s_raw[C::LDS_BYTES];
-  __shared__ float s_sw[2][kMaxChunks];
+  __shared__ float s_sw[HV][kMaxChunks];
   __shared__ int64_t s_scan[C::NW];
   __shared__ int64_t s_tile[4];
   uint8_t* s_a = s_raw;                                               // [2][BM*BK]
   // per stage and 128-column half: sa[row][chunk] * sw[half][chunk]
-  float* s_scl = reinterpret_cast<float*>(s_raw + 2 * BM * BK);        // [2][2][BM]
+  float* s_scl = reinterpret_cast<float*>(s_raw + 2 * BM * BK);        // [2][HV][BM]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -645,7 +659,7 @@ __global__ __launch_bounds__(512) void gemm_ws_kernel(GemmProblem p, int64_t n_t
     const int64_t sr = p.a_rows ? p.a_rows[r] : r;
     sasrc = p.a_scale + sr * kchunks;
   }
-  for (int64_t i = tid; i < 2 * kchunks; i += C::THREADS) {
+  for (int64_t i = tid; i < HV * kchunks; i += C::THREADS) {
     const int hb = static_cast<int>(i / kchunks);
     const int64_t c = i - hb * kchunks;
     s_sw[hb][c] = wsbase[(DSMOE_WROW(hb * 128) / BK) * kchunks + c];
@@ -682,8 +696,8 @@ __global__ __launch_bounds__(512) void gemm_ws_kernel(GemmProblem p, int64_t n_t
     _Pragma("unroll") for (int i = 0; i < C::A_PER; ++i) if (aval[i])                       \
         *reinterpret_cast<u32x4*>(&s_a[(bb) * BM * BK + adst[i]]) = ra[set][i];              \
     if (tid < BM) {                                                                          \
-      s_scl[((bb) * 2 + 0) * BM + tid] = rsa[set] * s_sw[0][(cc)];                           \
-      s_scl[((bb) * 2 + 1) * BM + tid] = rsa[set] * s_sw[1][(cc)];                           \
+      _Pragma("unroll") for (int h = 0; h < HV; ++h)                                         \
+        s_scl[((bb) * HV + h) * BM + tid] = rsa[set] * s_sw[h][(cc)];                        \
     }                                                                                        \
   } while (0)
 
@@ -707,6 +721,9 @@ __global__ __launch_bounds__(512) void gemm_ws_kernel(GemmProblem p, int64_t n_t
   DSMOE_ASTORE(0, 0, 0);
   __syncthreads();
 
+  // 16-row slices of the tile that hold rows (wave-uniform); the MFMAs,
+  // operand reads and promotions of the slices past them are skipped
+  const int nti = __builtin_amdgcn_readfirstlane(static_cast<int>((row1 - row0 + 15) / 16));
   static_assert(SLOTS % AS == 0, "A register sets follow the chunk index");
   for (int64_t c0 = 0; c0 < kchunks; c0 += SLOTS) {
 #pragma unroll
@@ -720,7 +737,7 @@ __global__ __launch_bounds__(512) void gemm_ws_kernel(GemmProblem p, int64_t n_t
       DSMOE_WLOAD(min<int64_t>(c + C::D, kchunks - 1), (u + C::D) % SLOTS);
       if (c < kchunks) {
         const int buf = static_cast<int>(c & 1);
-        const float* scl = s_scl + (buf * 2 + my_half) * BM + (lane >> 4) * 4;
+        const float* scl = s_scl + (buf * HV + my_half) * BM + (lane >> 4) * 4;
         const i32x8 b0 = cat8(wr[u][0][0], wr[u][0][1]);
         const i32x8 b1 = cat8(wr[u][1][0], wr[u][1][1]);
         // Software pipeline over the row tiles: the LDS operands of tile i+1
@@ -741,12 +758,14 @@ __global__ __launch_bounds__(512) void gemm_ws_kernel(GemmProblem p, int64_t n_t
         DSMOE_FRAG(0);
 #pragma unroll
         for (int i = 0; i <= NI; ++i) {
-          if (i + 1 < NI) DSMOE_FRAG(i + 1);
-          if (i < NI) {
+          // slices at or past nti are skipped: step nti only promotes
+          // slice nti-1, later steps do nothing (wave-uniform branches)
+          if (i < NI && i < nti) {
+            if (i + 1 < NI) DSMOE_FRAG(i + 1);
             pr[i & 1][0] = mfma_chunk(fa[i & 1], b0);
             pr[i & 1][1] = mfma_chunk(fa[i & 1], b1);
           }
-          if (i > 0) {
+          if (i > 0 && i <= nti) {
             const int q = (i - 1) & 1, qs = (i - 1) % 3;
 #pragma unroll
             for (int r2 = 0; r2 < 4; ++r2) {
@@ -798,10 +817,11 @@ hipError_t launch_lds(const GemmProblem& p, hipStream_t s) {
 
 template <int BM, Epilogue EPI>
 hipError_t launch_ws(const GemmProblem& p, hipStream_t s) {
-  const int64_t n_tiles = (EPI == Epilogue::kSwiGLUQuant) ? (p.N / 2) / 128 : p.N / 256;
+  constexpr int NW = (EPI == Epilogue::kSwiGLUQuant) ? 8 : kWsStoreWaves;
+  const int64_t n_tiles = (EPI == Epilogue::kSwiGLUQuant) ? (p.N / 2) / 128 : p.N / (NW * 32);
   const int64_t blocks = pad_grid(((p.M_total + BM - 1) / BM + p.G) * n_tiles);
   if (blocks == 0) return hipSuccess;
-  gemm_ws_kernel<BM, EPI><<<dim3(static_cast<unsigned>(blocks)), 512, 0, s>>>(p, n_tiles);
+  gemm_ws_kernel<BM, NW, EPI><<<dim3(static_cast<unsigned>(blocks)), NW * 64, 0, s>>>(p, n_tiles);
   return hipGetLastError();
 }
 
