@@ -317,42 +317,91 @@ __global__ __launch_bounds__(1024) void offsets_kernel(const int32_t* __restrict
   }
 }
 
-// Block e lists the (token, k) entries that chose expert e, in token order,
-// with a block-wide ballot prefix count.  Entry i = t*K + k.
-__global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ topk_idx,
-                                                   const float* __restrict__ gates, int64_t T,
-                                                   int32_t E, int32_t K,
-                                                   const int32_t* __restrict__ offsets,
-                                                   int32_t* __restrict__ perm,
-                                                   int32_t* __restrict__ inv,
-                                                   float* __restrict__ row_gate,
-                                                   int32_t ext) {
-  __shared__ int32_t wave_cnt[4];
+// Block e lists the (token, k) entries that chose expert e, in token order.
+// Entry i = t*K + k.  The 1024 threads take slabs of 8192 entries, 8
+// consecutive entries each; a thread's matches get consecutive positions after
+// an exclusive scan of the per-thread match counts (within the wave by
+// shuffles, across the 16 waves through LDS).  The next slab is loaded before
+// the current one is scanned.  VEC: topk_idx is 16-byte aligned (two 16-byte
+// loads per thread), otherwise 4-byte loads.
+constexpr int kRankThreads = 1024;
+constexpr int kRankPer = 8;
+
+template <bool VEC>
+__device__ __forceinline__ void rank_load(const int32_t* __restrict__ topk_idx, int64_t first, int64_t n,
+                                          int32_t (&v)[kRankPer]) {
+  if (VEC && first + kRankPer <= n) {
+    const int4 a = *reinterpret_cast<const int4*>(topk_idx + first);
+    const int4 b = *reinterpret_cast<const int4*>(topk_idx + first + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int q = 0; q < kRankPer; ++q) v[q] = first + q < n ? topk_idx[first + q] : -1;
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kRankThreads) void rank_kernel(const int32_t* __restrict__ topk_idx,
+                                                            const float* __restrict__ gates, int64_t T,
+                                                            int32_t E, int32_t K,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ perm,
+                                                            int32_t* __restrict__ inv,
+                                                            float* __restrict__ row_gate,
+                                                            int32_t ext) {
+  constexpr int NW = kRankThreads / 64;
+  constexpr int64_t STEP = static_cast<int64_t>(kRankThreads) * kRankPer;
+  __shared__ int32_t wave_cnt[2][NW];
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n = T * K;
   int32_t base = offsets[e];
-  for (int64_t i0 = 0; i0 < n; i0 += 256) {
-    const int64_t i = i0 + tid;
-    const bool match = i < n && topk_idx[i] == e;
-    const uint64_t bal = __ballot(match);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_cnt[wave] = __popcll(bal);
+  int32_t cur[kRankPer];
+  rank_load<VEC>(topk_idx, static_cast<int64_t>(tid) * kRankPer, n, cur);
+  int par = 0;
+  for (int64_t i0 = 0; i0 < n; i0 += STEP) {
+    const int64_t first = i0 + static_cast<int64_t>(tid) * kRankPer;
+    uint32_t mask = 0;
+    int m = 0;
+#pragma unroll
+    for (int q = 0; q < kRankPer; ++q) {
+      const bool hit = cur[q] == e;
+      mask |= static_cast<uint32_t>(hit) << q;
+      m += hit;
+    }
+    if (i0 + STEP < n) rank_load<VEC>(topk_idx, first + STEP, n, cur);
+    int incl = m;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    if (lane == 63) wave_cnt[par][wave] = incl;
     __syncthreads();
-    int wbase = 0;
-    for (int w = 0; w < wave; ++w) wbase += wave_cnt[w];
-    const int total = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
-    if (match) {
-      const int32_t pos = base + wbase + before;
+    int wbase = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int c = wave_cnt[par][w];
+      wbase += w < wave ? c : 0;
+      total += c;
+    }
+    int32_t pos = base + wbase + incl - m;
+    while (mask) {
+      const int q = __builtin_ctz(mask);
+      mask &= mask - 1;
+      const int64_t i = first + q;
       perm[pos] = static_cast<int32_t>(i / K);
       inv[i] = pos;
       if (row_gate) row_gate[pos] = gates[i];
+      ++pos;
     }
     base += total;
-    __syncthreads();
+    par ^= 1;   // the other wave_cnt buffer: no second barrier per slab
   }
   if (ext) {  // identity rows for the shared expert: perm[T*K + t] = t
-    for (int64_t t = static_cast<int64_t>(e) * 256 + tid; t < T; t += static_cast<int64_t>(E) * 256)
+    for (int64_t t = static_cast<int64_t>(e) * kRankThreads + tid; t < T;
+         t += static_cast<int64_t>(E) * kRankThreads)
       perm[n + t] = static_cast<int32_t>(t);
   }
 }
@@ -426,8 +475,11 @@ hipError_t launch_permute(const int32_t* topk_idx, const float* gates, int64_t T
                           int32_t* inv, float* row_gate, int32_t* offsets_ext, hipStream_t s) {
   offsets_kernel<<<1, 1024, 0, s>>>(counts, E, offsets, offsets_ext, T);
   if (T == 0) return hipGetLastError();
-  rank_kernel<<<E, 256, 0, s>>>(topk_idx, gates, T, E, K, offsets, perm, inv, row_gate,
-                                offsets_ext != nullptr ? 1 : 0);
+  const int32_t ext = offsets_ext != nullptr ? 1 : 0;
+  if ((reinterpret_cast<uintptr_t>(topk_idx) & 15) == 0)
+    rank_kernel<true><<<E, kRankThreads, 0, s>>>(topk_idx, gates, T, E, K, offsets, perm, inv, row_gate, ext);
+  else
+    rank_kernel<false><<<E, kRankThreads, 0, s>>>(topk_idx, gates, T, E, K, offsets, perm, inv, row_gate, ext);
   return hipGetLastError();
 }
 

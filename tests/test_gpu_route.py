@@ -123,3 +123,36 @@ def test_bias_update_matches_oracle(T, K, E):
     d.update_bias(bt, dev(counts), T, K, 0.001)
     want = ob.update_bias(b, counts, T, K, 0.001)
     assert np.array_equal(host(bt).view(np.uint32), want.view(np.uint32))
+
+
+def test_permute_with_4_byte_aligned_topk_buffer():
+    """dsmoe_route requires only 4-byte alignment of its int32 buffers; with a
+    topk_idx buffer that is not 16-byte aligned the permutation reads the
+    entries one by one.  Same results as the oracle, over several 8192-entry
+    slabs and a ragged last one."""
+    import ctypes
+    d = _dsmoe()
+    T, E, G, Mg, K = 2500, 256, 8, 4, 8
+    r = np.random.default_rng(23)
+    z = (r.standard_normal((T, E)) * 0.7).astype(np.float32)
+    b = r.uniform(-0.01, 0.01, E).astype(np.float32)
+    want = orr.route(z, b, G, Mg, K)
+    counts, offsets, perm, inv = orr.permute(want["topk_idx"], E)
+    banner(f"route unaligned topk T={T}")
+    zt, bt = dev(z), dev(b)
+    topk_buf = torch.zeros((T * K + 4,), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    out = {n: torch.empty(s, dtype=torch.int32, device="cuda")
+           for n, s in (("counts", (E,)), ("offsets", (E + 1,)), ("perm", (T * K,)), ("inv", (T, K)))}
+    topk_ptr = ctypes.c_void_p(topk_buf.data_ptr() + 4)
+    st = d.lib.dsmoe_route(ctypes.c_void_p(zt.data_ptr()), ctypes.c_void_p(bt.data_ptr()), T, E, G, Mg, K,
+                           topk_ptr, ctypes.c_void_p(gates.data_ptr()),
+                           *[ctypes.c_void_p(out[n].data_ptr()) for n in ("counts", "offsets", "perm", "inv")],
+                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, d.lib.dsmoe_status_str(st)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(topk_buf)[1:1 + T * K].reshape(T, K), want["topk_idx"])
+    assert np.array_equal(host(out["counts"]), counts)
+    assert np.array_equal(host(out["offsets"]), offsets)
+    assert np.array_equal(host(out["perm"]), perm)
+    assert np.array_equal(host(out["inv"]), inv)
