@@ -80,7 +80,7 @@ Layout layout_for(const dsmoe_moe_desc& d, int64_t T) {
   L.row_gate = take(TK * 4);
   L.qa = take(rows1 * d.I);
   L.sa = take(rows1 * (d.I / 128) * 4);
-  L.o = take(TK * d.H * 4);
+  L.o = take(rows1 * d.H * 4);
   L.total = off;
   return L;
 }
@@ -332,7 +332,7 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
   DSMOE_MARK(6);
 
   if (d->n_shared) {
-    // down projection of the shared expert, with the combine in its epilogue
+    // down projection of the shared expert into rows T*K .. T*K+T-1 of o
     dsmoe::GemmProblem g3{};
     g3.a = qa;
     g3.a_scale = sa;
@@ -344,19 +344,15 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
     g3.w_scale = w->s2_sh;
     g3.N = H;
     g3.K = I;
-    g3.c = y;
+    g3.c = o;
     g3.c_f32 = f32out;
-    g3.o_routed = o;
-    g3.inv = inv;
-    g3.topk = K;
-    g3.row_base = T * K;
-    g3.epi = dsmoe::Epilogue::kCombine;
+    g3.epi = dsmoe::Epilogue::kStore;
     g3.row_limit = T * K + T;
     g3.rows_hint = T;
     DSMOE_TRY(dsmoe::launch_grouped_gemm(g3, st));
-  } else {
-    DSMOE_TRY(dsmoe::launch_combine(o, inv, T, K, H, y, f32out, st));
   }
+  // y[t] = shared row + routed rows in ascending k (float32 sums)
+  DSMOE_TRY(dsmoe::launch_combine(o, inv, T, K, H, d->n_shared ? T * K : -1, y, f32out, st));
   DSMOE_MARK(7);
 #undef DSMOE_MARK
 

@@ -148,8 +148,6 @@ inline int64_t pad_grid(int64_t blocks) {
 // columns of one row and writes it with 16-byte stores:
 //   kStore      c[row][col] = acc
 //   kGateStore  c[row][col] = acc * row_gate[row]
-//   kCombine    y[t][col] = acc + sum over k (ascending) of o[inv[t][k]][col],
-//               t = row - row_base, read with 16/32-byte loads
 template <int NI, int NJ, Epilogue EPI>
 __device__ __forceinline__ void epi_rows(const GemmProblem& p, const f32x4 (&acc)[NI][NJ],
                                          int64_t row0, int64_t row1, int row_base, int64_t col0,
@@ -177,46 +175,17 @@ __device__ __forceinline__ void epi_rows(const GemmProblem& p, const f32x4 (&acc
     __builtin_amdgcn_wave_barrier();
     if (row < row1) {
       const int64_t col = col0 + lc;
-      int64_t orow = row;
       if constexpr (EPI == Epilogue::kGateStore) {
         const float gsc = p.row_gate[row];
 #pragma unroll
         for (int e = 0; e < PER; ++e) v[e] = v[e] * gsc;
       }
-      if constexpr (EPI == Epilogue::kCombine) {
-        orow = row - p.row_base;   // the token
-        const int32_t K_ = p.topk;
-        const int32_t* inv_t = p.inv + orow * K_;
-        for (int k = 0; k < K_; ++k) {
-          const int64_t src = inv_t[k];
-          if (p.c_f32) {
-            const f32x4* o4p = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.o_routed) + src * N + col);
-#pragma unroll
-            for (int q = 0; q < PER / 4; ++q) {
-              const f32x4 o4 = o4p[q];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[4 * q + e] = v[4 * q + e] + o4[e];
-            }
-          } else {
-            const u32x4* o8p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.o_routed) + src * N + col);
-#pragma unroll
-            for (int q = 0; q < PER / 8; ++q) {
-              const u32x4 o8 = o8p[q];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                v[8 * q + 2 * e] = v[8 * q + 2 * e] + __uint_as_float(o8[e] << 16);
-                v[8 * q + 2 * e + 1] = v[8 * q + 2 * e + 1] + __uint_as_float(o8[e] & 0xFFFF0000u);
-              }
-            }
-          }
-        }
-      }
       if (p.c_f32) {
-        f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(p.c) + orow * N + col);
+        f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(p.c) + row * N + col);
 #pragma unroll
         for (int q = 0; q < PER / 4; ++q) dst[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
       } else {
-        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.c) + orow * N + col);
+        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.c) + row * N + col);
 #pragma unroll
         for (int q = 0; q < PER / 8; ++q) {
           u32x4 w;
@@ -837,45 +806,79 @@ hipError_t launch_ws_bm(const GemmProblem& p, int bm, hipStream_t s) {
   }
 }
 
-// y[t][n] = sum over k of o[inv[t][k]][n] (layers without a shared expert);
-// float32 sum in ascending k, 8 columns per thread.
+// y[t][n] = o[shared0 + t][n] (when there is a shared expert) + sum over k,
+// ascending, of o[inv[t][k]][n]; float32 sums, 8 columns per thread read with
+// 16-byte loads (two for float32 rows).
+template <bool kF32>
+__device__ __forceinline__ void load_row8(const void* __restrict__ o, int64_t off, float (&v)[8]) {
+  if (kF32) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + off);
+    const f32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a[e];
+      v[4 + e] = b[e];
+    }
+  } else {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(o) + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(w[e] << 16);
+      v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+  }
+}
+
 template <bool kF32>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o,
                                                       const int32_t* __restrict__ inv, int64_t T,
-                                                      int32_t K, int64_t H, void* __restrict__ y) {
+                                                      int32_t K, int64_t H, int64_t shared0,
+                                                      void* __restrict__ y) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t per_row = H / 8;
   if (idx >= T * per_row) return;
   const int64_t t = idx / per_row;
   const int64_t c0 = (idx - t * per_row) * 8;
-  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < K; ++k) {
-    const int64_t r = inv[t * K + k];
-    for (int e = 0; e < 8; ++e) {
-      const float x = kF32 ? static_cast<const float*>(o)[r * H + c0 + e]
-                           : bf16_to_f32(static_cast<const uint16_t*>(o)[r * H + c0 + e]);
-      v[e] = (k == 0) ? x : v[e] + x;
-    }
+  const int32_t* inv_t = inv + t * K;
+  float v[8];
+  int k0 = 0;
+  if (shared0 >= 0) {
+    load_row8<kF32>(o, (shared0 + t) * H + c0, v);
+  } else {
+    load_row8<kF32>(o, static_cast<int64_t>(inv_t[0]) * H + c0, v);
+    k0 = 1;
   }
-  for (int e = 0; e < 8; ++e) {
-    if (kF32)
-      static_cast<float*>(y)[t * H + c0 + e] = v[e];
-    else
-      static_cast<uint16_t*>(y)[t * H + c0 + e] = f32_to_bf16(v[e]);
+  for (int k = k0; k < K; ++k) {
+    float u[8];
+    load_row8<kF32>(o, static_cast<int64_t>(inv_t[k]) * H + c0, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] + u[e];
+  }
+  if (kF32) {
+    f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(y) + t * H + c0);
+    dst[0] = f32x4{v[0], v[1], v[2], v[3]};
+    dst[1] = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = static_cast<uint32_t>(f32_to_bf16(v[2 * e])) |
+             (static_cast<uint32_t>(f32_to_bf16(v[2 * e + 1])) << 16);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + t * H + c0) = w;
   }
 }
 
 }  // namespace
 
 hipError_t launch_combine(const void* o, const int32_t* inv, int64_t T, int32_t K, int64_t H,
-                          void* y, bool f32, hipStream_t s) {
+                          int64_t shared0, void* y, bool f32, hipStream_t s) {
   const int64_t threads = T * (H / 8);
   if (threads == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
   if (f32)
-    combine_kernel<true><<<grid, 256, 0, s>>>(o, inv, T, K, H, y);
+    combine_kernel<true><<<grid, 256, 0, s>>>(o, inv, T, K, H, shared0, y);
   else
-    combine_kernel<false><<<grid, 256, 0, s>>>(o, inv, T, K, H, y);
+    combine_kernel<false><<<grid, 256, 0, s>>>(o, inv, T, K, H, shared0, y);
   return hipGetLastError();
 }
 
@@ -901,7 +904,6 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t s) {
     switch (p.epi) {
       case Epilogue::kStore: return launch_ws_bm<Epilogue::kStore>(p, bm, s);
       case Epilogue::kGateStore: return launch_ws_bm<Epilogue::kGateStore>(p, bm, s);
-      case Epilogue::kCombine: return launch_ws_bm<Epilogue::kCombine>(p, bm, s);
       case Epilogue::kSwiGLUQuant: return launch_ws_bm<Epilogue::kSwiGLUQuant>(p, bm, s);
     }
   }
@@ -911,9 +913,6 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t s) {
     case Epilogue::kGateStore:
       return wide ? launch_lds<256, Epilogue::kGateStore>(p, s)
                   : launch_lds<128, Epilogue::kGateStore>(p, s);
-    case Epilogue::kCombine:
-      return wide ? launch_lds<256, Epilogue::kCombine>(p, s)
-                  : launch_lds<128, Epilogue::kCombine>(p, s);
     case Epilogue::kSwiGLUQuant:
       return launch_lds<256, Epilogue::kSwiGLUQuant>(p, s);
   }

@@ -39,7 +39,6 @@ enum class Epilogue : int {
   kStore = 0,      // c[r][n] = acc (bf16 or f32)
   kGateStore = 1,  // c[r][n] = acc * row_gate[r]
   kSwiGLUQuant = 2,// h = [gate | up] -> a = silu(gate) * up -> 1x128 FP8 codes + scales
-  kCombine = 3,    // y[t][n] = acc + sum_k o[inv[t][k]][n]  (shared expert rows)
 };
 
 struct GemmProblem {
@@ -60,16 +59,14 @@ struct GemmProblem {
   Epilogue epi;
   const float* row_gate;     // kGateStore
   float* c_scale;            // kSwiGLUQuant: [M_total][N/2/128]
-  const void* o_routed;      // kCombine: [T*K][N], same dtype as c
-  const int32_t* inv;        // kCombine: [T][K]
-  int32_t topk;              // kCombine
-  int64_t row_base;          // kCombine: output row r is token r - row_base
   int64_t row_limit;         // rows >= row_limit are never read or written
   int64_t rows_hint;         // typical rows per group (selects the kernel shape)
 };
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t s);
+// y[t] = o[shared0 + t] (if shared0 >= 0) + sum over k ascending of
+// o[inv[t][k]]; o and y bf16 or f32 (f32), rows of H columns, H % 8 == 0.
 hipError_t launch_combine(const void* o, const int32_t* inv, int64_t T, int32_t K, int64_t H,
-                          void* y, bool f32, hipStream_t s);
+                          int64_t shared0, void* y, bool f32, hipStream_t s);
 
 }  // namespace dsmoe
