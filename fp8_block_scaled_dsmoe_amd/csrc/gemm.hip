@@ -654,11 +654,15 @@ void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
       wr[slot][j][1] = *reinterpret_cast<const u32x4*>(wsrc[j] + (cc) * BK + 16);            \
     }                                                                                        \
   } while (0)
+  // (A_SEGS and BM are multiples of 64, so whether a thread's segment i or
+  // row scale exists is the same for its whole wave: waves skip the loads
+  // they do not use)
 #define DSMOE_ALOAD(cc, set)                                                                 \
   do {                                                                                       \
-    _Pragma("unroll") for (int i = 0; i < C::A_PER; ++i) ra[set][i] =                        \
-        *reinterpret_cast<const u32x4*>(asrc[i] + (cc) * BK);                                \
-    rsa[set] = sasrc[(cc)];                                                                  \
+    _Pragma("unroll") for (int i = 0; i < C::A_PER; ++i)                                     \
+      if (C::THREADS * i + wave * 64 < C::A_SEGS)                                            \
+        ra[set][i] = *reinterpret_cast<const u32x4*>(asrc[i] + (cc) * BK);                   \
+    if (wave * 64 < BM) rsa[set] = sasrc[(cc)];                                              \
   } while (0)
 #define DSMOE_ASTORE(bb, set, cc)                                                            \
   do {                                                                                       \

@@ -152,3 +152,33 @@ def test_grouped_tile_shapes(mean_rows):
                                out_dtype=dt)
         want, dn = og.grouped_gemm(qa, sa, a_rows, offsets, qw, sw)
         assert_normalised_close(host(c), want, dn, TOL[dt], f"grouped mean {mean_rows} {dt}")
+
+
+@pytest.mark.parametrize("K", [640, 2048])
+def test_grouped_blocks_run_several_tiles(K):
+    """More tiles than blocks that fit on the GPU at once, so that blocks of
+    the weight-streaming kernel run several tiles each (the next tile's first
+    chunks are loaded during the previous tile's epilogue).  K = 640 gives 5
+    chunks, which does not divide the register ring; groups of ~100 rows,
+    some empty, some longer than one tile; gathered A rows."""
+    d = _dsmoe()
+    r = np.random.default_rng(K)
+    G, N = 72, 2048
+    sizes = r.poisson(100, size=G)
+    sizes[::9] = 0
+    sizes[5] = 400
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    m_total = int(offsets[-1])
+    rows_a = m_total + 7
+    qa = _codes(r, (rows_a, K))
+    sa = (np.ldexp(1.0, r.integers(-8, -2, size=(rows_a, K // 128))) *
+          r.uniform(1, 2, size=(rows_a, K // 128))).astype(np.float32)
+    qw = _codes(r, (G, N, K))
+    sw = np.ldexp(1.0, r.integers(-12, -6, size=(G, N // 128, K // 128))).astype(np.float32)
+    a_rows = r.permutation(rows_a)[:m_total].astype(np.int32)
+    banner(f"gemm grouped several tiles per block G={G} N={N} K={K} rows={m_total}")
+    want, dn = og.grouped_gemm(qa, sa, a_rows, offsets, qw, sw)
+    for dt in (torch.float32, torch.bfloat16):
+        c = d.fp8_grouped_gemm(dev(qa), dev(sa), dev(offsets), dev(qw), dev(sw), a_rows=dev(a_rows),
+                               out_dtype=dt)
+        assert_normalised_close(host(c), want, dn, TOL[dt], f"grouped several tiles K={K} {dt}")
