@@ -555,10 +555,14 @@ struct WsCfg {
   // loop; the SwiGLU epilogue reuses it for the gate/up exchange (f32), the
   // row maxima and the codes, the row-wise epilogues for one 16 x 32 f32
   // slice per wave
+  // The tile's A row scales for every chunk follow ([SA_CHUNKS max][BM] f32)
+  // when K allows (see the kernel).
   static constexpr int MAIN_BYTES = 2 * BM * BK + 2 * HALVES * BM * 4;
+  static constexpr int SA_CHUNKS = 64;
+  static constexpr int K_BYTES = MAIN_BYTES + SA_CHUNKS * BM * 4;
   static constexpr int EPI_BYTES = SWIGLU ? BM * 128 * 4 + 8 * BM * 4 + BM * 128 : 0;
   static constexpr int ROWS_BYTES = NW * 16 * 32 * 4;
-  static constexpr int MAX_A = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+  static constexpr int MAX_A = K_BYTES > EPI_BYTES ? K_BYTES : EPI_BYTES;
   static constexpr int LDS_BYTES = MAX_A > ROWS_BYTES ? MAX_A : ROWS_BYTES;
 };
 
@@ -577,6 +581,7 @@ void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
   uint8_t* s_a = s_raw;                                               // [2][BM*BK]
   // per stage and 128-column half: sa[row][chunk] * sw[half][chunk]
   float* s_scl = reinterpret_cast<float*>(s_raw + 2 * BM * BK);        // [2][HV][BM]
+  float* s_sa = reinterpret_cast<float*>(s_raw + C::MAIN_BYTES);       // [kchunks][BM]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -636,6 +641,29 @@ void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
   const int my_half = (wave * 32) / 128;
 #undef DSMOE_WROW
 
+  // The tile's A row scales for all chunks, staged once into LDS (16 lanes
+  // per row, 16-byte loads) instead of one scattered 4-byte load per row per
+  // chunk; needs K <= 64 chunks, a multiple of 4 chunks, and a 16-byte
+  // aligned scale buffer (uniform, else the per-chunk loads stay).
+  const bool stage_sa = kchunks <= C::SA_CHUNKS && (kchunks & 3) == 0 &&
+                        (reinterpret_cast<uintptr_t>(p.a_scale) & 15) == 0;
+  // (loaded here, stored to LDS after the prologue's loads are issued, so
+  // that the wait for them does not wait for the weight chunks)
+  constexpr int SA_PASSES = (BM + C::THREADS / 16 - 1) / (C::THREADS / 16);
+  f32x4 sv[SA_PASSES];
+  if (stage_sa) {
+#pragma unroll
+    for (int q = 0; q < SA_PASSES; ++q) {
+      const int lr = q * (C::THREADS / 16) + (tid >> 4), part = tid & 15;
+      sv[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (lr < BM && part * 4 < kchunks) {
+        const int64_t r = row0 + lr < row1 ? row0 + lr : row0;
+        const int64_t sr = p.a_rows ? p.a_rows[r] : r;
+        sv[q] = *reinterpret_cast<const f32x4*>(p.a_scale + sr * kchunks + part * 4);
+      }
+    }
+  }
+
   // Register sets: W chunks rotate through SLOTS sets (D ahead), A chunks
   // through A_SETS sets.  Loads of a wave complete in order, so the wait for
   // A(c+1) before it is stored to LDS at the end of iteration c also waits for
@@ -662,15 +690,16 @@ void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
     _Pragma("unroll") for (int i = 0; i < C::A_PER; ++i)                                     \
       if (C::THREADS * i + wave * 64 < C::A_SEGS)                                            \
         ra[set][i] = *reinterpret_cast<const u32x4*>(asrc[i] + (cc) * BK);                   \
-    if (wave * 64 < BM) rsa[set] = sasrc[(cc)];                                              \
+    if (!stage_sa && wave * 64 < BM) rsa[set] = sasrc[(cc)];                                 \
   } while (0)
 #define DSMOE_ASTORE(bb, set, cc)                                                            \
   do {                                                                                       \
     _Pragma("unroll") for (int i = 0; i < C::A_PER; ++i) if (aval[i])                       \
         *reinterpret_cast<u32x4*>(&s_a[(bb) * BM * BK + adst[i]]) = ra[set][i];              \
     if (tid < BM) {                                                                          \
+      const float as_ = stage_sa ? s_sa[(cc) * BM + tid] : rsa[set];                         \
       _Pragma("unroll") for (int h = 0; h < HV; ++h)                                         \
-        s_scl[((bb) * HV + h) * BM + tid] = rsa[set] * s_sw[h][(cc)];                        \
+        s_scl[((bb) * HV + h) * BM + tid] = as_ * s_sw[h][(cc)];                             \
     }                                                                                        \
   } while (0)
 
@@ -690,6 +719,15 @@ void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
   if constexpr (AS == 2) DSMOE_ALOAD(min<int64_t>(1, kchunks - 1), 1);
 #pragma unroll
   for (int d = 1; d < C::D; ++d) DSMOE_WLOAD(min<int64_t>(d, kchunks - 1), d);
+  if (stage_sa) {
+#pragma unroll
+    for (int q = 0; q < SA_PASSES; ++q) {
+      const int lr = q * (C::THREADS / 16) + (tid >> 4), part = tid & 15;
+      if (lr < BM && part * 4 < kchunks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_sa[(part * 4 + e) * BM + lr] = sv[q][e];
+    }
+  }
   __syncthreads();
   DSMOE_ASTORE(0, 0, 0);
   __syncthreads();
