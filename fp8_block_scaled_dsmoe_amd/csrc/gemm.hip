@@ -605,11 +605,17 @@ void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
 #define DSMOE_WROW(lc) (w_row_base + (lc) + ((lc) >= 128 ? w_up_shift : 0))
 
   // this wave's W columns: local [32*wave, 32*wave + 32), two 16-column
-  // tiles; lane reads row 16j + lane%16, bytes 32*(lane/16) .. +32 of a chunk
+  // tiles; lane reads row 16j + lane%16, bytes 16g .. 16g+15 and 64+16g ..
+  // 64+16g+15 of a chunk, g = lane/16.  (The MFMA sums over its 128 K slots in
+  // any order, so any split of the chunk's bytes over the four lane groups
+  // works when A uses the same one.  With this split each 16-byte load
+  // instruction covers one contiguous 64-byte half of each of its 16 rows'
+  // 128-byte lines, so a chunk costs one request per half line; splitting
+  // into 32-byte runs per group made each instruction touch both halves.)
   const uint8_t* wsrc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    wsrc[j] = wbase + DSMOE_WROW(wave * 32 + j * 16 + (lane & 15)) * K + (lane >> 4) * 32;
+    wsrc[j] = wbase + DSMOE_WROW(wave * 32 + j * 16 + (lane & 15)) * K + (lane >> 4) * 16;
   // A: BM rows x 8 segments per chunk, A_PER segments per thread
   const uint8_t* asrc[C::A_PER];
   int adst[C::A_PER];
@@ -679,7 +685,7 @@ void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
   do {                                                                                       \
     _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                          \
       wr[slot][j][0] = *reinterpret_cast<const u32x4*>(wsrc[j] + (cc) * BK);                 \
-      wr[slot][j][1] = *reinterpret_cast<const u32x4*>(wsrc[j] + (cc) * BK + 16);            \
+      wr[slot][j][1] = *reinterpret_cast<const u32x4*>(wsrc[j] + (cc) * BK + 64);            \
     }                                                                                        \
   } while (0)
   // (A_SEGS and BM are multiples of 64, so whether a thread's segment i or
@@ -710,7 +716,7 @@ void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int frow = lane & 15;
-  const int fseg = (lane >> 4) * 2;
+  const int fseg = lane >> 4;   // the A fragment takes 16-byte segments fseg and fseg + 4
 
   // prologue: A chunks 0 .. AS-1 and W chunks 0 .. D-1 in flight; A chunk 0
   // staged (the weight-block scales were staged above)
@@ -763,7 +769,7 @@ void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
   do {                                                                                          \
     const int r_ = (ii) * 16 + frow;                                                            \
     fa[(ii) & 1] = cat8(*reinterpret_cast<const u32x4*>(&s_a[buf * BM * BK + swz(r_, fseg)]),   \
-                        *reinterpret_cast<const u32x4*>(&s_a[buf * BM * BK + swz(r_, fseg + 1)])); \
+                        *reinterpret_cast<const u32x4*>(&s_a[buf * BM * BK + swz(r_, fseg + 4)])); \
     ps[(ii) % 3] = *reinterpret_cast<const f32x4*>(scl + (ii) * 16);                           \
   } while (0)
         DSMOE_FRAG(0);
