@@ -534,6 +534,15 @@ __global__ __launch_bounds__(2 * BN) void gemm_lds_kernel(GemmProblem p, int64_t
 #define DSMOE_WS_STORE_WAVES 8
 #endif
 constexpr int kWsStoreWaves = DSMOE_WS_STORE_WAVES;
+#ifndef DSMOE_WS_WT
+#define DSMOE_WS_WT 1
+#endif
+// Weight chunks are loaded a full 128-byte line per 8 lanes and reach the
+// MFMA operand layout through a small per-wave LDS transpose (see the kernel).
+constexpr bool kWsWt = DSMOE_WS_WT != 0;
+#ifndef DSMOE_WS_WT_SLOTS
+#define DSMOE_WS_WT_SLOTS 2
+#endif
 
 template <int BM, int NW_, bool SWIGLU>
 struct WsCfg {
@@ -548,7 +557,10 @@ struct WsCfg {
   // keep one set so that their register count allows four waves per SIMD
   // (two blocks per CU), which doubles their weight bytes in flight instead.
   static constexpr int A_SETS = (BM >= 64 && NW == 8) ? 2 : 1;
-  static constexpr int SLOTS = D + 1;            // W register sets
+  // W register sets: with the LDS transpose a set is free once its chunk is
+  // in LDS (the chunk before it is computed), so D sets keep D chunks in flight
+  static constexpr int SLOTS = kWsWt ? DSMOE_WS_WT_SLOTS : D + 1;
+  static constexpr int UNROLL = SLOTS % A_SETS == 0 ? SLOTS : SLOTS * A_SETS;
   static constexpr int A_SEGS = BM * 8;          // 16-byte segments of one A chunk
   static constexpr int A_PER = (A_SEGS + THREADS - 1) / THREADS;
   // LDS: two A stages + the row scales of each 128-column half during the K
@@ -559,7 +571,8 @@ struct WsCfg {
   // when K allows (see the kernel).
   static constexpr int MAIN_BYTES = 2 * BM * BK + 2 * HALVES * BM * 4;
   static constexpr int SA_CHUNKS = 64;
-  static constexpr int K_BYTES = MAIN_BYTES + SA_CHUNKS * BM * 4;
+  static constexpr int WT_BYTES = kWsWt ? NW * 32 * BK : 0;   // one chunk of 32 rows per wave
+  static constexpr int K_BYTES = MAIN_BYTES + SA_CHUNKS * BM * 4 + WT_BYTES;
   static constexpr int EPI_BYTES = SWIGLU ? BM * 128 * 4 + 8 * BM * 4 + BM * 128 : 0;
   static constexpr int ROWS_BYTES = NW * 16 * 32 * 4;
   static constexpr int MAX_A = K_BYTES > EPI_BYTES ? K_BYTES : EPI_BYTES;
@@ -616,6 +629,28 @@ void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     wsrc[j] = wbase + DSMOE_WROW(wave * 32 + j * 16 + (lane & 15)) * K + (lane >> 4) * 16;
+  // Transposed path: load q (0..3) of a chunk reads rows 8q .. 8q+7 of the
+  // wave's 32, a whole 128-byte line per 8 lanes (lane: row 8q + lane/8, bytes
+  // 16*(lane%8)); byte offsets within the group's weight matrix (< 2^32).
+  // The wave writes the chunk to its LDS area, 16-byte piece s of local row
+  // 8q + rb at piece slot s ^ f(rb, q), f = (rb >> 1) | ((q & 1) << 2): with
+  // it both the writes (lanes 16k..16k+15: two rows x 8 pieces) and the
+  // fragment reads (16 rows, one piece) hit 16 different 4-bank groups.
+  // (A wave's 32 rows lie in one half of the SwiGLU column layout, so load q
+  // is load 0 moved by the uniform 8q rows.  The other LDS addresses follow
+  // from one per lane: q odd adds 1 KB and flips bit 2 of the piece slot,
+  // i.e. address bit 6, which is 0 in the rest of the address; piece g + 4
+  // likewise differs from piece g in that bit alone; q + 2 and j + 1 are 2 KB
+  // further.)
+  uint32_t woff0 = 0;
+  int wt_w0 = 0, wt_r0 = 0;
+  if constexpr (kWsWt) {
+    woff0 = static_cast<uint32_t>(DSMOE_WROW(wave * 32 + (lane >> 3)) * K + (lane & 7) * 16);
+    const int rbw = lane >> 3, sw_ = lane & 7;
+    wt_w0 = wave * 32 * BK + rbw * 128 + ((sw_ ^ (rbw >> 1)) * 16);
+    const int rbr = lane & 7, qpr = (lane & 15) >> 3, g = lane >> 4;
+    wt_r0 = wave * 32 * BK + qpr * 1024 + rbr * 128 + ((g ^ ((rbr >> 1) | (qpr << 2))) * 16);
+  }
   // A: BM rows x 8 segments per chunk, A_PER segments per thread
   const uint8_t* asrc[C::A_PER];
   int adst[C::A_PER];
@@ -678,14 +713,21 @@ void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
   // across the barrier; with one set it was issued in iteration c, after
   // W(c+2), and only W(c+3) does.
   constexpr int AS = C::A_SETS;
-  u32x4 wr[SLOTS][2][2];
+  u32x4 wr[SLOTS][2][2];   // transposed path: [slot][q >> 1][q & 1] = load q
   u32x4 ra[AS][C::A_PER];
   float rsa[AS];
+  uint8_t* s_w = s_raw + C::MAIN_BYTES + C::SA_CHUNKS * BM * 4;
 #define DSMOE_WLOAD(cc, slot)                                                                \
   do {                                                                                       \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                          \
-      wr[slot][j][0] = *reinterpret_cast<const u32x4*>(wsrc[j] + (cc) * BK);                 \
-      wr[slot][j][1] = *reinterpret_cast<const u32x4*>(wsrc[j] + (cc) * BK + 64);            \
+    if constexpr (kWsWt) {                                                                   \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q)                                          \
+        wr[slot][q >> 1][q & 1] =                                                            \
+            *reinterpret_cast<const u32x4*>(wbase + (cc) * BK + q * 8 * K + woff0);          \
+    } else {                                                                                 \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                        \
+        wr[slot][j][0] = *reinterpret_cast<const u32x4*>(wsrc[j] + (cc) * BK);               \
+        wr[slot][j][1] = *reinterpret_cast<const u32x4*>(wsrc[j] + (cc) * BK + 64);          \
+      }                                                                                      \
     }                                                                                        \
   } while (0)
   // (A_SEGS and BM are multiples of 64, so whether a thread's segment i or
@@ -724,7 +766,7 @@ void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
   DSMOE_WLOAD(0, 0);
   if constexpr (AS == 2) DSMOE_ALOAD(min<int64_t>(1, kchunks - 1), 1);
 #pragma unroll
-  for (int d = 1; d < C::D; ++d) DSMOE_WLOAD(min<int64_t>(d, kchunks - 1), d);
+  for (int d = 1; d < (kWsWt ? SLOTS : C::D); ++d) DSMOE_WLOAD(min<int64_t>(d, kchunks - 1), d);
   if (stage_sa) {
 #pragma unroll
     for (int q = 0; q < SA_PASSES; ++q) {
@@ -741,22 +783,44 @@ void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
   // 16-row slices of the tile that hold rows (wave-uniform); the MFMAs,
   // operand reads and promotions of the slices past them are skipped
   const int nti = __builtin_amdgcn_readfirstlane(static_cast<int>((row1 - row0 + 15) / 16));
-  static_assert(SLOTS % AS == 0, "A register sets follow the chunk index");
-  for (int64_t c0 = 0; c0 < kchunks; c0 += SLOTS) {
+  static_assert(C::UNROLL % AS == 0 && C::UNROLL % SLOTS == 0, "register sets follow the chunk index");
+  for (int64_t c0 = 0; c0 < kchunks; c0 += C::UNROLL) {
 #pragma unroll
-    for (int u = 0; u < SLOTS; ++u) {
+    for (int u = 0; u < C::UNROLL; ++u) {
       const int64_t c = c0 + u;
       const int64_t cn = min<int64_t>(c + 1, kchunks - 1);
       // loads are issued unconditionally (clamped to the last chunk) so every
       // register set is written on every path; set u % AS held A(c), which
-      // is in LDS already
+      // is in LDS already.  The A load goes first: the wait for A(c+1) at the
+      // end of the iteration then leaves the later weight chunks in flight.
       DSMOE_ALOAD(min<int64_t>(c + AS, kchunks - 1), u % AS);
-      DSMOE_WLOAD(min<int64_t>(c + C::D, kchunks - 1), (u + C::D) % SLOTS);
+      i32x8 b0, b1;
+      if constexpr (kWsWt) {
+        // W(c) (set u % SLOTS) to this wave's LDS area, then that set takes
+        // W(c + SLOTS); the fragments come back in the MFMA layout
+        const int sl = u % SLOTS;
+        if (c < kchunks) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<u32x4*>(s_w + ((q & 1) ? ((wt_w0 + 1024) ^ 64) : wt_w0) + (q >> 1) * 2048) =
+                wr[sl][q >> 1][q & 1];
+        }
+        DSMOE_WLOAD(min<int64_t>(c + SLOTS, kchunks - 1), sl);
+        if (c < kchunks) {
+          const int wt_r1 = wt_r0 ^ 64;
+          b0 = cat8(*reinterpret_cast<const u32x4*>(s_w + wt_r0),
+                    *reinterpret_cast<const u32x4*>(s_w + wt_r1));
+          b1 = cat8(*reinterpret_cast<const u32x4*>(s_w + wt_r0 + 2048),
+                    *reinterpret_cast<const u32x4*>(s_w + wt_r1 + 2048));
+        }
+      } else {
+        DSMOE_WLOAD(min<int64_t>(c + C::D, kchunks - 1), (u + C::D) % SLOTS);
+        b0 = cat8(wr[u % SLOTS][0][0], wr[u % SLOTS][0][1]);
+        b1 = cat8(wr[u % SLOTS][1][0], wr[u % SLOTS][1][1]);
+      }
       if (c < kchunks) {
         const int buf = static_cast<int>(c & 1);
         const float* scl = s_scl + (buf * HV + my_half) * BM + (lane >> 4) * 4;
-        const i32x8 b0 = cat8(wr[u][0][0], wr[u][0][1]);
-        const i32x8 b1 = cat8(wr[u][1][0], wr[u][1][1]);
         // Software pipeline over the row tiles: the LDS operands of tile i+1
         // are requested before the MFMAs of tile i are issued, and tile i-1
         // is promoted after them.  Operands, partial sums and scales rotate
