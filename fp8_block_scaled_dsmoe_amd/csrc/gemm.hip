@@ -64,11 +64,17 @@ __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
 }
 
 // Map a logical tile index to (group, column tile, row range).  Tiles are
-// numbered group by group; inside a group, column tile by column tile, and
-// inside a column tile, row tile by row tile.  The row tiles that share one
-// weight tile are therefore adjacent, run on the same XCD at the same time and
-// read that weight tile from HBM once (the second one hits L2).  s_out gets
-// {group, row0, row1, column tile}; returns false past the end.
+// numbered group by group.  Inside a group the row tiles form bands of
+// kRowBand; a band is numbered column tile by column tile, and inside a
+// column tile row tile by row tile.  An XCD's run of 32 consecutive tiles is
+// therefore (for a tall group) 4 row tiles x 8 column tiles, which share their
+// A rows and weight tiles through that XCD's L2; with one tile per column
+// (32 row tiles sharing a weight tile) every A row was fetched from HBM once
+// per column tile.  Groups of at most kRowBand row tiles are one band: their
+// row tiles that share a weight tile stay adjacent.  s_out gets {group, row0,
+// row1, column tile}; returns false past the end.
+constexpr int64_t kRowBand = 4;
+
 template <int THREADS, int TILE_M>
 __device__ bool decode_tile(const int32_t* __restrict__ offsets, int32_t G, int64_t logical,
                             int64_t n_tiles, int64_t* s_scan, int64_t* s_out) {
@@ -105,8 +111,11 @@ __device__ bool decode_tile(const int32_t* __restrict__ offsets, int32_t G, int6
     const int64_t excl = incl - mine;
     if (mine > 0 && logical >= excl && logical < incl) {
       const int64_t local = logical - excl;
-      const int64_t nt = local / cnt;
-      const int64_t r0 = lo + (local - nt * cnt) * TILE_M;
+      const int64_t band = local / (kRowBand * n_tiles);
+      const int64_t in_band = local - band * kRowBand * n_tiles;
+      const int64_t rows_in_band = min<int64_t>(kRowBand, cnt - band * kRowBand);
+      const int64_t nt = in_band / rows_in_band;
+      const int64_t r0 = lo + (band * kRowBand + in_band - nt * rows_in_band) * TILE_M;
       s_out[0] = g;
       s_out[1] = r0;
       s_out[2] = min<int64_t>(r0 + TILE_M, hi);
@@ -528,6 +537,209 @@ __global__ __launch_bounds__(2 * BN) void gemm_lds_kernel(GemmProblem p, int64_t
 }
 
 // ===========================================================================
+// gemm_lds2_kernel: 256 x 256 tiles for groups of many rows (MFMA-bound)
+// ===========================================================================
+// Eight waves as 4 (rows) x 2 (columns), each owning 64 rows x 128 columns
+// (4 x 8 MFMA tiles, 128 accumulator registers).  A and W chunks (32 KB each)
+// come HBM -> LDS by DMA into two stages; per chunk a wave reads its 4 A
+// fragments once and streams its 8 W fragments, 0.75 KB of LDS per MFMA
+// (the 64 x 64 waves of the 128-row kernel read 1 KB).  The chunk's 32
+// MFMAs run as one sequence in which each step issues one MFMA and promotes
+// the one issued two steps earlier, so LDS reads, MFMAs and promotions
+// overlap; partial sums rotate through a three-deep ring.  A wave whose 64
+// rows all lie past the tile's rows skips its reads, MFMAs and promotions
+// (finer, per-slice guards cost the schedule its registers: the
+// accumulators spilled).
+constexpr int L2BM = 256;
+#ifndef DSMOE_LDS2
+#define DSMOE_LDS2 1
+#endif
+constexpr bool kUseLds2 = DSMOE_LDS2 != 0;
+
+struct Lds2Cfg {
+  static constexpr int THREADS = 512;
+  static constexpr int NW = 8;
+  static constexpr int BN = 256;
+  static constexpr int A_WLOADS = L2BM * BK / 1024;   // 32 wave-loads of 1 KB per chunk
+  static constexpr int B_WLOADS = BN * BK / 1024;     // 32
+  static constexpr int PER_WAVE = (A_WLOADS + B_WLOADS) / NW;
+  static constexpr int ROWS_PER_WAVE = L2BM / NW;      // 1x128 scales staged per wave
+  static constexpr int STAGE_BYTES = (L2BM + BN) * BK;
+  static_assert(ROWS_PER_WAVE <= 64, "one scale load per lane");
+};
+
+template <Epilogue EPI>
+__global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n_tiles) {
+  using C = Lds2Cfg;
+  constexpr int THREADS = C::THREADS;
+  constexpr int BN = C::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_stage[2][C::STAGE_BYTES];   // [A | W] per stage
+  __shared__ __attribute__((aligned(256))) float s_sa[2][L2BM];
+  __shared__ float s_sw[2][kMaxChunks];
+  __shared__ int64_t s_scan[THREADS / 64];
+  __shared__ int64_t s_tile[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int64_t logical = xcd_logical_block();
+  if (!decode_tile<THREADS, L2BM>(p.offsets, p.G, logical, n_tiles, s_scan, s_tile)) return;
+  const int32_t g = static_cast<int32_t>(s_tile[0]);
+  const int64_t nt = s_tile[3];
+  const int64_t row0 = s_tile[1];
+  const int64_t row1 = min(s_tile[2], p.row_limit);
+  if (row0 >= row1) return;
+
+  const int64_t K = p.K, N = p.N;
+  const int64_t kchunks = K / BK;
+  const bool last = (p.w_last != nullptr) && (g == p.G - 1);
+  const uint8_t* wbase = last ? p.w_last : p.w + static_cast<int64_t>(g) * N * K;
+  const float* wsbase = last ? p.w_scale_last : p.w_scale + static_cast<int64_t>(g) * (N / BK) * kchunks;
+  const int64_t w_row_base = (EPI == Epilogue::kSwiGLUQuant) ? nt * 128 : nt * BN;
+  const int64_t w_up_shift = (EPI == Epilogue::kSwiGLUQuant) ? N / 2 - 128 : 0;
+#define DSMOE_WROW(lc) (w_row_base + (lc) + ((lc) >= 128 ? w_up_shift : 0))
+
+  // Waves 0-3 copy the A chunk, waves 4-7 the W chunk: wave-load jj covers
+  // tile rows 8jj .. 8jj+7 (lane -> row 8jj + lane/8, physical segment lane%8
+  // holding logical segment (lane%8) ^ swz_key(row); swz_key(row) is
+  // (lane/8) ^ (jj & 1) for these rows).  A waves keep the gathered row of
+  // each of their loads (32-bit); W rows are a uniform base plus lane/8.
+  constexpr int A_WAVES = C::A_WLOADS / C::PER_WAVE;
+  const bool a_wave = wave < A_WAVES;
+  int32_t arow[C::PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::PER_WAVE; ++i) {
+    const int row = (wave * C::PER_WAVE + i) * 8 + (lane >> 3);
+    const int64_t r = row0 + row < row1 ? row0 + row : row0;
+    arow[i] = a_wave ? static_cast<int32_t>(p.a_rows ? p.a_rows[r] : r) : 0;
+  }
+  const int64_t w_lane = static_cast<int64_t>(lane >> 3) * K;
+  const float* sa_src;
+  {
+    const int row = wave * C::ROWS_PER_WAVE + (lane < C::ROWS_PER_WAVE ? lane : 0);
+    const int64_t r = row0 + row < row1 ? row0 + row : row0;
+    const int64_t sr = p.a_rows ? p.a_rows[r] : r;
+    sa_src = p.a_scale + sr * kchunks;
+  }
+  for (int64_t i = tid; i < 2 * kchunks; i += THREADS) {
+    const int hb = static_cast<int>(i / kchunks);
+    const int64_t c = i - hb * kchunks;
+    s_sw[hb][c] = wsbase[(DSMOE_WROW(hb * 128) / BK) * kchunks + c];
+  }
+#undef DSMOE_WROW
+  __syncthreads();
+
+  const uint32_t st_base = lds_addr(&s_stage[0][0]);
+  const uint32_t sa_base = lds_addr(&s_sa[0][0]) + 4 * wave * C::ROWS_PER_WAVE;
+#define DSMOE_ISSUE(cc, st)                                                                  \
+  do {                                                                                       \
+    if (a_wave) {                                                                            \
+      _Pragma("unroll") for (int i = 0; i < C::PER_WAVE; ++i) {                              \
+        const int jj = wave * C::PER_WAVE + i;                                               \
+        const int lseg = (lane & 7) ^ (lane >> 3) ^ (jj & 1);                                \
+        dma_16(p.a + static_cast<int64_t>(arow[i]) * K + (cc) * BK + lseg * 16,              \
+               __builtin_amdgcn_readfirstlane(st_base + (st) * C::STAGE_BYTES + jj * 1024)); \
+      }                                                                                      \
+    } else {                                                                                 \
+      _Pragma("unroll") for (int i = 0; i < C::PER_WAVE; ++i) {                              \
+        const int jj = (wave - A_WAVES) * C::PER_WAVE + i;                                   \
+        const int lseg = (lane & 7) ^ (lane >> 3) ^ (jj & 1);                                \
+        const int64_t wr0 = w_row_base + jj * 8 + (jj * 8 >= 128 ? w_up_shift : 0);          \
+        dma_16(wbase + wr0 * K + w_lane + (cc) * BK + lseg * 16,                             \
+               __builtin_amdgcn_readfirstlane(st_base + (st) * C::STAGE_BYTES + L2BM * BK + jj * 1024)); \
+      }                                                                                      \
+    }                                                                                        \
+    if (lane < C::ROWS_PER_WAVE)                                                             \
+      dma_4(sa_src + (cc), __builtin_amdgcn_readfirstlane(sa_base + (st) * (L2BM * 4)));      \
+  } while (0)
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int frow = lane & 15;
+  const int fseg = (lane >> 4) * 2;
+  // whether any of this wave's 64 rows is a row of the tile (wave-uniform)
+  const int nsl = __builtin_amdgcn_readfirstlane(static_cast<int>(row1 - row0 > wm * 64));
+
+  DSMOE_ISSUE(0, 0);
+  for (int64_t c = 0; c < kchunks; ++c) {
+    const int buf = static_cast<int>(c & 1);
+    wait_vmcnt<0>();  // this wave's copies of chunk c landed
+    block_barrier();  // everyone's did; everyone is done with chunk c-1 (the other stage)
+    if (c + 1 < kchunks) DSMOE_ISSUE(c + 1, buf ^ 1);
+    if (nsl > 0) {
+      const uint8_t* sa_ = &s_stage[buf][0];
+      const uint8_t* sb_ = &s_stage[buf][L2BM * BK];
+      const float sw = s_sw[wn][c];
+      i32x8 fa[4];
+      float scl[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 64 + i * 16 + frow;
+        fa[i] = cat8(*reinterpret_cast<const u32x4*>(sa_ + swz(r, fseg)),
+                     *reinterpret_cast<const u32x4*>(sa_ + swz(r, fseg + 1)));
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(&s_sa[buf][wm * 64 + i * 16 + (lane >> 4) * 4]);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) scl[i][rr] = s4[rr] * sw;
+      }
+      i32x8 bf[2];
+      f32x4 part[3];
+#define DSMOE_BFRAG(jj)                                                                        \
+  do {                                                                                         \
+    const int r_ = wn * 128 + (jj) * 16 + frow;                                                \
+    bf[(jj) & 1] = cat8(*reinterpret_cast<const u32x4*>(sb_ + swz(r_, fseg)),                  \
+                        *reinterpret_cast<const u32x4*>(sb_ + swz(r_, fseg + 1)));             \
+  } while (0)
+      // The chunk's 32 MFMAs in one sequence k = 4j + i (W fragment j, row
+      // slice i); step k issues MFMA k and promotes MFMA k-2, whose result
+      // two MFMAs (64 cycles of the matrix pipe) cover; partial sums rotate
+      // through three register sets.  W fragment j+1 is read at the start of
+      // column j.
+      DSMOE_BFRAG(0);
+#pragma unroll
+      for (int k = 0; k < 34; ++k) {
+        const int j = k >> 2, i = k & 3;
+        if (k < 32) {
+          if (i == 0 && j + 1 < 8) DSMOE_BFRAG(j + 1);
+          part[k % 3] = mfma_chunk(fa[i], bf[j & 1]);
+        }
+        if (k >= 2) {
+          const int kp = k - 2, jp = kp >> 2, ip = kp & 3;
+          {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              acc[ip][jp][rr] = __builtin_fmaf(part[kp % 3][rr], scl[ip][rr], acc[ip][jp][rr]);
+          }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#undef DSMOE_BFRAG
+    }
+  }
+#undef DSMOE_ISSUE
+  __syncthreads();  // all waves are done with the stages (the epilogues reuse them)
+
+  if constexpr (EPI != Epilogue::kSwiGLUQuant) {
+    epi_rows<4, 8, EPI>(p, acc, row0, row1, wm * 64, nt * BN + wn * 128,
+                        reinterpret_cast<float*>(&s_stage[0][0]) + wave * 16 * 128);
+  } else {  // wn = 0 waves hold the 128 gate columns, wn = 1 the matching up columns
+    // s_ex [4 pairs][2][4][4][64] f32x4 = 128 KB; the codes reuse its start
+    // (the exchange is read before the barrier that precedes the codes)
+    epi_swiglu<4, 8, L2BM, 2>(p, acc, row0, row1, wm * 64, wn == 0, wm, wn, 0, nt,
+                              reinterpret_cast<f32x4*>(&s_stage[0][0]), &s_sa[0][0],
+                              &s_stage[0][0]);
+  }
+}
+
+// ===========================================================================
 // gemm_ws_kernel: weight streaming for groups of few rows
 // ===========================================================================
 #ifndef DSMOE_WS_STORE_WAVES
@@ -896,6 +1108,15 @@ hipError_t launch_lds(const GemmProblem& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <Epilogue EPI>
+hipError_t launch_lds2(const GemmProblem& p, hipStream_t s) {
+  const int64_t n_tiles = (EPI == Epilogue::kSwiGLUQuant) ? (p.N / 2) / 128 : p.N / Lds2Cfg::BN;
+  const int64_t blocks = pad_grid(((p.M_total + L2BM - 1) / L2BM + p.G) * n_tiles);
+  if (blocks == 0) return hipSuccess;
+  gemm_lds2_kernel<EPI><<<dim3(static_cast<unsigned>(blocks)), Lds2Cfg::THREADS, 0, s>>>(p, n_tiles);
+  return hipGetLastError();
+}
+
 template <int BM, Epilogue EPI>
 hipError_t launch_ws(const GemmProblem& p, hipStream_t s) {
   constexpr int NW = (EPI == Epilogue::kSwiGLUQuant) ? 8 : kWsStoreWaves;
@@ -1017,6 +1238,13 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t s) {
       case Epilogue::kStore: return launch_ws_bm<Epilogue::kStore>(p, bm, s);
       case Epilogue::kGateStore: return launch_ws_bm<Epilogue::kGateStore>(p, bm, s);
       case Epilogue::kSwiGLUQuant: return launch_ws_bm<Epilogue::kSwiGLUQuant>(p, bm, s);
+    }
+  }
+  if (kUseLds2 && wide) {
+    switch (p.epi) {
+      case Epilogue::kStore: return launch_lds2<Epilogue::kStore>(p, s);
+      case Epilogue::kGateStore: return launch_lds2<Epilogue::kGateStore>(p, s);
+      case Epilogue::kSwiGLUQuant: return launch_lds2<Epilogue::kSwiGLUQuant>(p, s);
     }
   }
   switch (p.epi) {
