@@ -126,10 +126,10 @@ def test_dense_full_size_sampled_rows(dt):
     assert_normalised_close(host(c)[rows], want, dn, TOL[dt], f"dense full size {dt}")
 
 
-@pytest.mark.parametrize("mean_rows", [3, 20, 30, 70, 90, 120, 400])
+@pytest.mark.parametrize("mean_rows", [3, 12, 20, 42, 62, 82, 105, 114, 400])
 def test_grouped_tile_shapes(mean_rows):
     """Group sizes around each row-tile height the library picks (weight
-    streaming with 16/32/64/96/128/160-row tiles, and the 128-row LDS
+    streaming with 16/32/64/96/128/160/176/192-row tiles, and the 256-row LDS
     kernel), including empty groups and groups longer than one tile."""
     d = _dsmoe()
     r = np.random.default_rng(mean_rows)
