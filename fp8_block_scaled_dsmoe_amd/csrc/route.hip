@@ -464,7 +464,9 @@ hipError_t launch_route_select(const float* logits, const float* bias, int64_t T
                                float* gates, int32_t* counts, hipStream_t s) {
   fill_i32_kernel<<<(E + 255) / 256, 256, 0, s>>>(counts, E, 0);
   if (T == 0) return hipGetLastError();
-  const int waves = (17 * static_cast<int64_t>(E) * 4 <= 65536) ? 16 : 8;
+  // 16 tokens per block for large batches (fewer atomics on hot experts), 4
+  // for small ones (more blocks in flight: 64 tokens in 4 blocks were slower)
+  const int waves = T < 1024 ? 4 : (17 * static_cast<int64_t>(E) * 4 <= 65536) ? 16 : 8;
   const dim3 grid(static_cast<unsigned>((T + waves - 1) / waves));
   const dim3 block(waves * 64);
   const size_t lds = sizeof(float) * (waves + 1) * static_cast<size_t>(E);
@@ -474,8 +476,11 @@ hipError_t launch_route_select(const float* logits, const float* bias, int64_t T
     if (waves == 16)                                                                               \
       route_select_kernel<SL, 16><<<grid, block, lds, s>>>(logits, bias, T, E, G, Mg, K, topk_idx, \
                                                            gates, counts);                         \
-    else                                                                                           \
+    else if (waves == 8)                                                                           \
       route_select_kernel<SL, 8><<<grid, block, lds, s>>>(logits, bias, T, E, G, Mg, K, topk_idx,  \
+                                                          gates, counts);                          \
+    else                                                                                           \
+      route_select_kernel<SL, 4><<<grid, block, lds, s>>>(logits, bias, T, E, G, Mg, K, topk_idx,  \
                                                           gates, counts);                          \
   } while (0)
   if (slots <= 1)
