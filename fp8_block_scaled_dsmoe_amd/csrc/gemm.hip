@@ -605,7 +605,10 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   // tile rows 8jj .. 8jj+7 (lane -> row 8jj + lane/8, physical segment lane%8
   // holding logical segment (lane%8) ^ swz_key(row); swz_key(row) is
   // (lane/8) ^ (jj & 1) for these rows).  A waves keep the gathered row of
-  // each of their loads (32-bit); W rows are a uniform base plus lane/8.
+  // each of their loads (32-bit) and form the 64-bit address at issue time:
+  // eight precomputed addresses did not fit, and reloading a spilled one
+  // waits for every outstanding copy (vmcnt(0)), serialising the chunk's
+  // copies.  W rows are a uniform base plus lane/8.
   constexpr int A_WAVES = C::A_WLOADS / C::PER_WAVE;
   const bool a_wave = wave < A_WAVES;
   int32_t arow[C::PER_WAVE];
@@ -639,7 +642,9 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
       _Pragma("unroll") for (int i = 0; i < C::PER_WAVE; ++i) {                              \
         const int jj = wave * C::PER_WAVE + i;                                               \
         const int lseg = (lane & 7) ^ (lane >> 3) ^ (jj & 1);                                \
-        dma_16(p.a + static_cast<int64_t>(arow[i]) * K + (cc) * BK + lseg * 16,              \
+        int32_t ar = arow[i];                                                                \
+        asm volatile("" : "+v"(ar));  /* address formed here, not kept live across chunks */ \
+        dma_16(p.a + static_cast<int64_t>(ar) * K + (cc) * BK + lseg * 16,                   \
                __builtin_amdgcn_readfirstlane(st_base + (st) * C::STAGE_BYTES + jj * 1024)); \
       }                                                                                      \
     } else {                                                                                 \
