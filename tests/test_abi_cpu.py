@@ -98,6 +98,8 @@ def test_gemm_validation_errors():
     assert L.dsmoe_fp8_grouped_gemm(a, a, None, None, 1, 64, a, a, 128, 128, a, 0, None) == 1
     assert L.dsmoe_fp8_grouped_gemm(a, a, None, a, 1, 64, _vp(MISALIGNED), a, 128, 128, a, 0, None) == 3
     assert L.dsmoe_fp8_grouped_gemm(None, None, None, None, 1, 0, None, None, 128, 128, None, 0, None) == 0
+    # the contraction length is at most 32768 (256 chunks of 128)
+    assert L.dsmoe_fp8_grouped_gemm(a, a, None, a, 1, 64, a, a, 128, 32768 + 128, a, 0, None) == 2
 
 
 def test_moe_forward_validation_errors():

@@ -65,6 +65,25 @@ def test_dense_random_codes(M, N, K, dt):
     assert_normalised_close(host(c), want, dn, TOL[dt], f"dense {M}x{N}x{K} {dt}")
 
 
+# Long contractions: 65 chunks (the weight-streaming kernel's row scales are
+# then loaded per chunk instead of staged once per tile) and the 256-chunk
+# maximum, on the weight-streaming kernel (few rows) and the 256 x 256 kernel.
+@pytest.mark.parametrize("M,N,K", [(40, 256, 8320), (600, 512, 8320), (40, 256, 32768), (300, 256, 32768)])
+def test_dense_long_k(M, N, K):
+    d = _dsmoe()
+    r = np.random.default_rng(M + N + K)
+    qa, qw = _codes(r, (M, K)), _codes(r, (N, K))
+    sa = (np.ldexp(1.0, r.integers(-8, -2, size=(M, K // 128))) *
+          r.uniform(1, 2, size=(M, K // 128))).astype(np.float32)
+    sw = np.ldexp(1.0, r.integers(-12, -6, size=(N // 128, K // 128))).astype(np.float32)
+    banner(f"gemm dense long K M={M} N={N} K={K}")
+    c = d.fp8_grouped_gemm(dev(qa), dev(sa), dev(np.array([0, M], np.int32)), dev(qw[None]),
+                           dev(sw[None]), out_dtype=torch.float32)
+    want = og.block_scaled_gemm(qa, sa, qw, sw)
+    dn = og.gemm_normaliser(qa, sa, qw, sw)
+    assert_normalised_close(host(c), want, dn, TOL[torch.float32], f"dense {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
 def test_dense_outlier_inputs(dt):
     d = _dsmoe()

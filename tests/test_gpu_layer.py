@@ -257,3 +257,10 @@ def test_v3_prefill_full_size_sampled():
 
 def test_v3_decode_full_size_sampled():
     _v3_case("v3_decode", n_sample=4, out_dtype=torch.float32)
+
+
+def test_v3_skew_full_size_sampled():
+    # Zipf(1.1) expert popularity: the hot experts' groups (thousands of rows)
+    # run on 256 x 256 tiles, the tail on weight-streaming tiles
+    g = _v3_case("v3_skew", n_sample=4)
+    assert g["counts"].max() > 8 * g["counts"].mean()
