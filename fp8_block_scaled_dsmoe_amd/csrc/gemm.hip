@@ -238,14 +238,18 @@ __device__ __forceinline__ void epi_swiglu(const GemmProblem& p, const f32x4 (&a
   const int frow = lane & 15;
   f32x4* ex_gate = s_ex + ((pair * 2 + 0) * NI * HJ) * 64;   // gate values for the up wave
   f32x4* ex_up = s_ex + ((pair * 2 + 1) * NI * HJ) * 64;     // up values for the gate wave
+  // (a bitwise select of two values read at constant indices: written as a
+  // branch, the compiler selected between the two accumulator addresses,
+  // which moved the accumulators to scratch memory)
+  const uint32_t keep_g = is_gate ? 0xffffffffu : 0u;
+  f32x4* ex_mine = is_gate ? ex_gate : ex_up;
 #pragma unroll
   for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < HJ; ++j) {
-      if (is_gate)
-        ex_gate[(i * HJ + j) * 64 + lane] = acc[i][HJ + j];
-      else
-        ex_up[(i * HJ + j) * 64 + lane] = acc[i][j];
+      const u32x4 g_ = __builtin_bit_cast(u32x4, acc[i][HJ + j]);
+      const u32x4 u_ = __builtin_bit_cast(u32x4, acc[i][j]);
+      ex_mine[(i * HJ + j) * 64 + lane] = __builtin_bit_cast(f32x4, (g_ & keep_g) | (u_ & ~keep_g));
     }
   __syncthreads();
   float av[NI][HJ][4];
