@@ -157,11 +157,25 @@ inline int64_t pad_grid(int64_t blocks) {
 // columns of one row and writes it with 16-byte stores:
 //   kStore      c[row][col] = acc
 //   kGateStore  c[row][col] = acc * row_gate[row]
+// The scratch rows are NCOL + 4 floats apart, so the 4-byte writes, whose
+// 16-lane groups are 4 rows apart, land 16 banks apart and do not conflict.
+// Rows NCOL floats apart made them 4-way conflicted.  The reads (4 lanes per
+// row) go from 8-way to 2-way conflicts at 128 columns, from 4-way to none at
+// 64, and stay 2-way at 32.  The 256 x 256 kernel's epilogue took 7.5 us per
+// tile before.  Reading one row per lane of a 16-lane phase would remove the
+// remaining read conflicts, but each quad of lanes then stores to four rows,
+// and the weight-streaming kernel's down projection got 3% slower.
+template <int NJ>
+constexpr int epi_rows_stride() { return 16 * NJ + 4; }
+template <int NJ>
+constexpr int epi_rows_scratch_floats() { return 16 * epi_rows_stride<NJ>(); }
+
 template <int NI, int NJ, Epilogue EPI>
 __device__ __forceinline__ void epi_rows(const GemmProblem& p, const f32x4 (&acc)[NI][NJ],
                                          int64_t row0, int64_t row1, int row_base, int64_t col0,
                                          float* scratch) {
   constexpr int NCOL = 16 * NJ;
+  constexpr int S = epi_rows_stride<NJ>();
   constexpr int PER = NCOL / 4;  // columns per lane
   const int lane = threadIdx.x & 63;
   const int64_t N = p.N;
@@ -171,7 +185,7 @@ __device__ __forceinline__ void epi_rows(const GemmProblem& p, const f32x4 (&acc
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        scratch[((lane >> 4) * 4 + r) * NCOL + j * 16 + (lane & 15)] = acc[i][j][r];
+        scratch[((lane >> 4) * 4 + r) * S + j * 16 + (lane & 15)] = acc[i][j][r];
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
     const int lr = lane >> 2;
@@ -179,7 +193,7 @@ __device__ __forceinline__ void epi_rows(const GemmProblem& p, const f32x4 (&acc
     const int64_t row = row0 + row_base + i * 16 + lr;
     float v[PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) v[e] = scratch[lr * NCOL + lc + e];
+    for (int e = 0; e < PER; ++e) v[e] = scratch[lr * S + lc + e];
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_wave_barrier();
     if (row < row1) {
@@ -531,8 +545,9 @@ __global__ __launch_bounds__(2 * BN) void gemm_lds_kernel(GemmProblem p, int64_t
   __syncthreads();  // all waves are done with the staging buffers (epilogues reuse them)
 
   if constexpr (EPI != Epilogue::kSwiGLUQuant) {
+    static_assert(C::NW * epi_rows_scratch_floats<4>() * 4 <= sizeof(s_a), "epilogue scratch fits the stages");
     epi_rows<4, 4, EPI>(p, acc, row0, row1, wm * 64, nt * BN + wn * 64,
-                        reinterpret_cast<float*>(&s_a[0][0]) + wave * 16 * 64);
+                        reinterpret_cast<float*>(&s_a[0][0]) + wave * epi_rows_scratch_floats<4>());
   } else {  // waves with wn 0,1 hold gate columns, 2,3 the matching up columns
     epi_swiglu<4, 4, LBM, 4>(p, acc, row0, row1, wm * 64, wn < 2, wm * 2 + (wn & 1), wn, (wn & 1) * 64,
                              nt, reinterpret_cast<f32x4*>(&s_b[0][0]),
@@ -737,8 +752,9 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   __syncthreads();  // all waves are done with the stages (the epilogues reuse them)
 
   if constexpr (EPI != Epilogue::kSwiGLUQuant) {
+    static_assert(C::NW * epi_rows_scratch_floats<8>() * 4 <= sizeof(s_stage), "epilogue scratch fits the stages");
     epi_rows<4, 8, EPI>(p, acc, row0, row1, wm * 64, nt * BN + wn * 128,
-                        reinterpret_cast<float*>(&s_stage[0][0]) + wave * 16 * 128);
+                        reinterpret_cast<float*>(&s_stage[0][0]) + wave * epi_rows_scratch_floats<8>());
   } else {  // wn = 0 waves hold the 128 gate columns, wn = 1 the matching up columns
     // s_ex [4 pairs][2][4][4][64] f32x4 = 128 KB; the codes reuse its start
     // (the exchange is read before the barrier that precedes the codes)
@@ -795,7 +811,7 @@ struct WsCfg {
   static constexpr int WT_BYTES = kWsWt ? NW * 32 * BK : 0;   // one chunk of 32 rows per wave
   static constexpr int K_BYTES = MAIN_BYTES + SA_CHUNKS * BM * 4 + WT_BYTES;
   static constexpr int EPI_BYTES = SWIGLU ? BM * 128 * 4 + 8 * BM * 4 + BM * 128 : 0;
-  static constexpr int ROWS_BYTES = NW * 16 * 32 * 4;
+  static constexpr int ROWS_BYTES = NW * epi_rows_scratch_floats<2>() * 4;
   static constexpr int MAX_A = K_BYTES > EPI_BYTES ? K_BYTES : EPI_BYTES;
   static constexpr int LDS_BYTES = MAX_A > ROWS_BYTES ? MAX_A : ROWS_BYTES;
 };
@@ -1098,7 +1114,7 @@ void gemm_ws_kernel(GemmProblem p, int64_t n_tiles) {
 
   if constexpr (EPI != Epilogue::kSwiGLUQuant) {
     epi_rows<NI, 2, EPI>(p, acc, row0, row1, 0, nt * C::BN + wave * 32,
-                         reinterpret_cast<float*>(s_raw) + wave * 16 * 32);
+                         reinterpret_cast<float*>(s_raw) + wave * epi_rows_scratch_floats<2>());
   } else {  // waves 0-3 hold gate columns 32w.., waves 4-7 the matching up columns (pairs w, w+4)
     epi_swiglu<NI, 2, BM, 8>(p, acc, row0, row1, 0, wave < 4, wave & 3, wave, (wave & 3) * 32, nt,
                              reinterpret_cast<f32x4*>(s_raw),
