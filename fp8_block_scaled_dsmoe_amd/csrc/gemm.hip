@@ -645,13 +645,6 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
     const int64_t sr = p.a_rows ? p.a_rows[r] : r;
     sa_src = p.a_scale + sr * kchunks;
   }
-  for (int64_t i = tid; i < 2 * kchunks; i += THREADS) {
-    const int hb = static_cast<int>(i / kchunks);
-    const int64_t c = i - hb * kchunks;
-    s_sw[hb][c] = wsbase[(DSMOE_WROW(hb * 128) / BK) * kchunks + c];
-  }
-#undef DSMOE_WROW
-  __syncthreads();
 
   const uint32_t st_base = lds_addr(&s_stage[0][0]);
   const uint32_t sa_base = lds_addr(&s_sa[0][0]) + 4 * wave * C::ROWS_PER_WAVE;
@@ -671,7 +664,9 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
         const int jj = (wave - A_WAVES) * C::PER_WAVE + i;                                   \
         const int lseg = (lane & 7) ^ (lane >> 3) ^ (jj & 1);                                \
         const int64_t wr0 = w_row_base + jj * 8 + (jj * 8 >= 128 ? w_up_shift : 0);          \
-        dma_16(wbase + wr0 * K + w_lane + (cc) * BK + lseg * 16,                             \
+        const uint8_t* wrow = wbase + wr0 * K + (cc) * BK;  /* wave-uniform */                \
+        asm volatile("" : "+s"(wrow));  /* formed here (scalar), not kept per lane */          \
+        dma_16(wrow + w_lane + lseg * 16,                                                    \
                __builtin_amdgcn_readfirstlane(st_base + (st) * C::STAGE_BYTES + L2BM * BK + jj * 1024)); \
       }                                                                                      \
     }                                                                                        \
@@ -690,7 +685,16 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   // whether any of this wave's 64 rows is a row of the tile (wave-uniform)
   const int nsl = __builtin_amdgcn_readfirstlane(static_cast<int>(row1 - row0 > wm * 64));
 
+  // chunk 0's copies first: they need no staged scale, so their latency
+  // overlaps the weight-block scale staging and its barrier
   DSMOE_ISSUE(0, 0);
+  for (int64_t i = tid; i < 2 * kchunks; i += THREADS) {
+    const int hb = static_cast<int>(i / kchunks);
+    const int64_t c = i - hb * kchunks;
+    s_sw[hb][c] = wsbase[(DSMOE_WROW(hb * 128) / BK) * kchunks + c];
+  }
+#undef DSMOE_WROW
+  __syncthreads();
   for (int64_t c = 0; c < kchunks; ++c) {
     const int buf = static_cast<int>(c & 1);
     wait_vmcnt<0>();  // this wave's copies of chunk c landed
