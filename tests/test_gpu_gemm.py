@@ -175,11 +175,10 @@ def test_grouped_tile_shapes(mean_rows):
 
 @pytest.mark.parametrize("K", [640, 2048])
 def test_grouped_blocks_run_several_tiles(K):
-    """More tiles than blocks that fit on the GPU at once, so that blocks of
-    the weight-streaming kernel run several tiles each (the next tile's first
-    chunks are loaded during the previous tile's epilogue).  K = 640 gives 5
-    chunks, which does not divide the register ring; groups of ~100 rows,
-    some empty, some longer than one tile; gathered A rows."""
+    """More tiles than blocks that fit on the GPU at once, so the launch runs
+    in several rounds of blocks.  K = 640 gives 5 chunks, which does not
+    divide the register ring; groups of ~100 rows, some empty, some longer
+    than one tile; gathered A rows."""
     d = _dsmoe()
     r = np.random.default_rng(K)
     G, N = 72, 2048
@@ -201,3 +200,28 @@ def test_grouped_blocks_run_several_tiles(K):
         c = d.fp8_grouped_gemm(dev(qa), dev(sa), dev(offsets), dev(qw), dev(sw), a_rows=dev(a_rows),
                                out_dtype=dt)
         assert_normalised_close(host(c), want, dn, TOL[dt], f"grouped several tiles K={K} {dt}")
+
+
+@pytest.mark.parametrize("G,mean_rows", [(1100, 3), (600, 260)])
+def test_grouped_many_groups(G, mean_rows):
+    """More groups than a block has threads, so the tile decoder's scan over
+    the group table takes several passes: 1100 groups of a few rows
+    (weight-streaming tiles) and 600 groups of ~260 rows (256 x 256 tiles),
+    with empty groups among them."""
+    d = _dsmoe()
+    r = np.random.default_rng(G)
+    N, K = 256, 256
+    sizes = r.poisson(mean_rows, size=G)
+    sizes[r.choice(G, size=G // 10, replace=False)] = 0
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    m_total = int(offsets[-1])
+    qa = _codes(r, (m_total, K))
+    sa = (np.ldexp(1.0, r.integers(-8, -2, size=(m_total, K // 128))) *
+          r.uniform(1, 2, size=(m_total, K // 128))).astype(np.float32)
+    qw = _codes(r, (G, N, K))
+    sw = np.ldexp(1.0, r.integers(-12, -6, size=(G, N // 128, K // 128))).astype(np.float32)
+    a_rows = np.arange(m_total, dtype=np.int32)
+    banner(f"gemm many groups G={G} rows={m_total}")
+    c = d.fp8_grouped_gemm(dev(qa), dev(sa), dev(offsets), dev(qw), dev(sw), out_dtype=torch.float32)
+    want, dn = og.grouped_gemm(qa, sa, a_rows, offsets, qw, sw)
+    assert_normalised_close(host(c), want, dn, TOL[torch.float32], f"grouped G={G}")
