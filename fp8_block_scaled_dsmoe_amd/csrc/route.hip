@@ -133,14 +133,27 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 }
 
 // z[t][e] = sum over splits s = 0, 1, ... of part[s][t][e], in that order;
-// 4 values per thread.
+// 4 values per thread.  The splits are loaded 8 at a time before they are
+// added (in the same order): one load per iteration waited for each load in
+// turn, and 28 splits at 64 tokens took 9.7 us.
 __global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part,
                                                             int32_t splits, int64_t n,
                                                             float* __restrict__ z) {
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
   if (i >= n) return;
   f32x4 v = *reinterpret_cast<const f32x4*>(part + i);
-  for (int32_t sp = 1; sp < splits; ++sp) {
+  int32_t sp = 1;
+  for (; sp + 8 <= splits; sp += 8) {
+    f32x4 u[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      u[q] = *reinterpret_cast<const f32x4*>(part + static_cast<int64_t>(sp + q) * n + i);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = v[r] + u[q][r];
+  }
+  for (; sp < splits; ++sp) {
     const f32x4 u = *reinterpret_cast<const f32x4*>(part + static_cast<int64_t>(sp) * n + i);
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = v[r] + u[r];
@@ -227,11 +240,28 @@ __global__ __launch_bounds__(WAVES * 64) void route_select_kernel(
     for (int n = 0; n < n_top; ++n) {
       float bv = 0.f;
       int bi = -1;
-      for (int q = 0; q < per_group; ++q) {
+      // (keys read 8 at a time, then compared in index order)
+      int q = 0;
+      for (; q + 8 <= per_group; q += 8) {
+        float kv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kv[u] = keys[lane * per_group + q + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = lane * per_group + q + u;
+          const float v = kv[u];
+          const bool after = (pi < 0) || (v < pv) || (v == pv && e > pi);
+          if (after && (bi < 0 || v > bv)) {  // strict > keeps the lowest index on ties
+            bv = v;
+            bi = e;
+          }
+        }
+      }
+      for (; q < per_group; ++q) {
         const int e = lane * per_group + q;
         const float v = keys[e];
         const bool after = (pi < 0) || (v < pv) || (v == pv && e > pi);
-        if (after && (bi < 0 || v > bv)) {  // strict > keeps the lowest index on ties
+        if (after && (bi < 0 || v > bv)) {
           bv = v;
           bi = e;
         }
