@@ -177,16 +177,55 @@ __device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
   return a.v > b.v || (a.v == b.v && a.i < b.i);
 }
 
+template <int CTRL>
+__device__ __forceinline__ Cand cand_dpp(const Cand& c) {
+  Cand d;
+  d.v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, c.v), CTRL, 0xF, 0xF, false));
+  d.i = __builtin_amdgcn_update_dpp(0, c.i, CTRL, 0xF, 0xF, false);
+  d.pay = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, c.pay), CTRL, 0xF, 0xF, false));
+  return d;
+}
+
+// The wave's best candidate, in every lane.  `better` is a strict total order
+// (value descending, index ascending; no candidate last), so any pairing of
+// lanes gives the same winner: within each 16-lane row DPP exchanges with
+// lane ^ 1, lane ^ 2, the mirrored lane in the 8-lane half and in the row;
+// then lane ^ 16 (ds_swizzle), and the two 32-lane halves' winners meet in
+// scalar registers.  (Six ds_bpermute rounds of three values made the 12
+// selection rounds of a token the latency of the selection kernel.)
 __device__ __forceinline__ Cand wave_best(Cand c) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    Cand d;
-    d.v = __shfl_xor(c.v, o, 64);
-    d.i = __shfl_xor(c.i, o, 64);
-    d.pay = __shfl_xor(c.pay, o, 64);
+  {
+    const Cand d = cand_dpp<0xB1>(c);   // quad_perm [1,0,3,2]: lane ^ 1
     if (better(d, c)) c = d;
   }
-  return c;
+  {
+    const Cand d = cand_dpp<0x4E>(c);   // quad_perm [2,3,0,1]: lane ^ 2
+    if (better(d, c)) c = d;
+  }
+  {
+    const Cand d = cand_dpp<0x141>(c);  // row_half_mirror: lane 7 - l within 8
+    if (better(d, c)) c = d;
+  }
+  {
+    const Cand d = cand_dpp<0x140>(c);  // row_mirror: lane 15 - l within 16
+    if (better(d, c)) c = d;
+  }
+  {
+    constexpr int kXor16 = (0x10 << 10) | 0x1F;   // ds_swizzle bit mode: lane ^ 16 within 32
+    Cand d;
+    d.v = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, c.v), kXor16));
+    d.i = __builtin_amdgcn_ds_swizzle(c.i, kXor16);
+    d.pay = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, c.pay), kXor16));
+    if (better(d, c)) c = d;
+  }
+  Cand lo, hi;
+  lo.v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c.v), 0));
+  lo.i = __builtin_amdgcn_readlane(c.i, 0);
+  lo.pay = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c.pay), 0));
+  hi.v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c.v), 32));
+  hi.i = __builtin_amdgcn_readlane(c.i, 32);
+  hi.pay = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c.pay), 32));
+  return better(hi, lo) ? hi : lo;
 }
 
 // One wave per token, WAVES tokens per block.  The block's choices are
