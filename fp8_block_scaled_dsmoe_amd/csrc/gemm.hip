@@ -1193,7 +1193,10 @@ __device__ __forceinline__ void load_row8(const void* __restrict__ o, int64_t of
   }
 }
 
-template <bool kF32>
+// KT > 0: K == KT known at compile time (8, the V3 top-K); the K row indices
+// and then all K rows are loaded before the sums, which keep their order.
+// With a runtime K each row waited for its index and then for itself.
+template <bool kF32, int KT>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o,
                                                       const int32_t* __restrict__ inv, int64_t T,
                                                       int32_t K, int64_t H, int64_t shared0,
@@ -1205,18 +1208,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o
   const int64_t c0 = (idx - t * per_row) * 8;
   const int32_t* inv_t = inv + t * K;
   float v[8];
-  int k0 = 0;
-  if (shared0 >= 0) {
-    load_row8<kF32>(o, (shared0 + t) * H + c0, v);
-  } else {
-    load_row8<kF32>(o, static_cast<int64_t>(inv_t[0]) * H + c0, v);
-    k0 = 1;
-  }
-  for (int k = k0; k < K; ++k) {
-    float u[8];
-    load_row8<kF32>(o, static_cast<int64_t>(inv_t[k]) * H + c0, u);
+  if constexpr (KT > 0) {
+    int32_t r[KT];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = v[e] + u[e];
+    for (int k = 0; k < KT; ++k) r[k] = inv_t[k];
+    float u[KT][8];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) load_row8<kF32>(o, static_cast<int64_t>(r[k]) * H + c0, u[k]);
+    int k0 = 0;
+    if (shared0 >= 0) {
+      load_row8<kF32>(o, (shared0 + t) * H + c0, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = u[0][e];
+      k0 = 1;
+    }
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+      if (k >= k0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = v[e] + u[k][e];
+      }
+  } else {
+    int k0 = 0;
+    if (shared0 >= 0) {
+      load_row8<kF32>(o, (shared0 + t) * H + c0, v);
+    } else {
+      load_row8<kF32>(o, static_cast<int64_t>(inv_t[0]) * H + c0, v);
+      k0 = 1;
+    }
+    for (int k = k0; k < K; ++k) {
+      float u[8];
+      load_row8<kF32>(o, static_cast<int64_t>(inv_t[k]) * H + c0, u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = v[e] + u[e];
+    }
   }
   if (kF32) {
     f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(y) + t * H + c0);
@@ -1239,10 +1265,17 @@ hipError_t launch_combine(const void* o, const int32_t* inv, int64_t T, int32_t 
   const int64_t threads = T * (H / 8);
   if (threads == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
-  if (f32)
-    combine_kernel<true><<<grid, 256, 0, s>>>(o, inv, T, K, H, shared0, y);
-  else
-    combine_kernel<false><<<grid, 256, 0, s>>>(o, inv, T, K, H, shared0, y);
+  if (K == 8) {
+    if (f32)
+      combine_kernel<true, 8><<<grid, 256, 0, s>>>(o, inv, T, K, H, shared0, y);
+    else
+      combine_kernel<false, 8><<<grid, 256, 0, s>>>(o, inv, T, K, H, shared0, y);
+  } else {
+    if (f32)
+      combine_kernel<true, 0><<<grid, 256, 0, s>>>(o, inv, T, K, H, shared0, y);
+    else
+      combine_kernel<false, 0><<<grid, 256, 0, s>>>(o, inv, T, K, H, shared0, y);
+  }
   return hipGetLastError();
 }
 
