@@ -2,6 +2,12 @@
 
     python bench.py [--steps K] [--warmup W] [--workload v3_prefill]
 
+The dense workload (--workload c2_dense) times one block-scaled FP8 GEMM
+instead: A [4096][7168] and B [7168][4096] (passed as W [4096][7168]) from the
+seeded recipe with 1% x50 outliers in A, quantised 1x128 / 128x128 on the
+GPU, then dsmoe_fp8_grouped_gemm with one group, timed with its inputs warm
+in the 256 MB MALL and with a 512 MB write between launches that evicts them.
+
 A step is one pass of the whole hot path over one batch: dsmoe_moe_forward
 (1x128 quantisation of x, router logits, group-limited top-8 routing,
 permute, gate/up FP8 GEMM with SwiGLU and requantisation, routed and shared
@@ -38,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="v3_prefill",
-                    choices=["v3_prefill", "v3_decode", "v3_skew", "tiny"])
+                    choices=["v3_prefill", "v3_decode", "v3_skew", "tiny", "c2_dense"])
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=10)
@@ -167,6 +173,104 @@ def cpu_baseline(cfg, n_tokens, torch, dsi):
     }
 
 
+def dense_cpu_baseline(a, w, n_rows):
+    """The oracle GEMM, as it stands, on the first n_rows rows of A (float64,
+    codes and scales from the oracle's own quantisers, untimed)."""
+    from oracle import gemm as og
+    from oracle import quant as oq
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    qa, sa = oq.quant_act_1x128(a[:n_rows])
+    qw, sw = oq.quant_w_128x128(w)
+    t0 = time.perf_counter()
+    og.block_scaled_gemm(qa, sa, qw, sw)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * n_rows * w.shape[0] * w.shape[1]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"the first {n_rows} rows of A through the oracle GEMM (float64 NumPy, "
+                      f"quantisation excluded), {dt:.1f} s"}
+
+
+def run_dense(args, torch):
+    import numpy as np
+    import fp8_block_scaled_dsmoe_amd as d
+    import dsmoe_inputs as dsi
+    M, N, K = 4096, 4096, 7168
+    out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+    log(f"workload c2_dense: M={M} N={N} K={K}, 1% x50 outliers in A, y {args.out_dtype}")
+    a, w = dsi.dense_gemm_inputs_host(M, N, K, seed=0)
+    a_dev = torch.from_numpy(a).to("cuda").to(torch.bfloat16)
+    w_dev = torch.from_numpy(w).to("cuda").to(torch.bfloat16)
+    qa, sa = d.quant_act_1x128(a_dev)
+    qw, sw = d.quant_w_128x128(w_dev)
+    offsets = torch.tensor([0, M], dtype=torch.int32, device="cuda")
+    c = torch.empty((M, N), dtype=out_dtype, device="cuda")
+    flush = torch.empty((512 << 20,), dtype=torch.uint8, device="cuda")
+
+    def gemm():
+        d.fp8_grouped_gemm(qa, sa, offsets, qw.unsqueeze(0), sw.unsqueeze(0), c=c)
+
+    def quant():
+        d.quant_act_1x128(a_dev, qa, sa)
+
+    for _ in range(args.warmup):
+        quant()
+        gemm()
+    torch.cuda.synchronize()
+
+    def timed(fn, flush_between):
+        ts = []
+        for _ in range(args.steps):
+            if flush_between:
+                flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    warm_ms = timed(gemm, False)
+    cold_ms = timed(gemm, True)
+    quant_ms = timed(quant, False)
+    flops = 2.0 * M * N * K
+    tf = flops / (warm_ms * 1e-3) / 1e12
+    tf_cold = flops / (cold_ms * 1e-3) / 1e12
+    log(f"GEMM {warm_ms * 1e3:.1f} us warm ({tf:.0f} TFLOP/s), {cold_ms * 1e3:.1f} us after a MALL flush "
+        f"({tf_cold:.0f} TFLOP/s); quantising A {quant_ms * 1e3:.1f} us")
+    result = {
+        "metric": METRIC,
+        "value": round(tf, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(warm_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"c2_dense: one block-scaled FP8 GEMM, M={M} N={N} K={K}, "
+                               f"A with 1% x50 outliers, 1x128 / 128x128 scales, y {args.out_dtype}",
+                   "M": M, "N": N, "K": K},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "kernel": "dense block-scaled FP8 GEMM (256 x 256 tiles)",
+                     "algorithmic_flops": flops, "avg_ms": round(warm_ms, 4)},
+        "mall_flushed": {"ms": round(cold_ms, 4), "tflops": round(tf_cold, 2),
+                         "frac": round(tf_cold / PEAK_FP8_TFLOPS, 4)},
+        "quant_a_ms": round(quant_ms, 4),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = dense_cpu_baseline(a, w, 64)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -176,6 +280,9 @@ def main():
     import torch
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.workload == "c2_dense":
+        run_dense(args, torch)
         return
     import fp8_block_scaled_dsmoe_amd as d
     import dsmoe_inputs as dsi
