@@ -8,6 +8,14 @@ seeded recipe with 1% x50 outliers in A, quantised 1x128 / 128x128 on the
 GPU, then dsmoe_fp8_grouped_gemm with one group, timed with its inputs warm
 in the 256 MB MALL and with a 512 MB write between launches that evicts them.
 
+The granularity workload (--workload c2_granularity) runs the same GEMM
+end to end from the bf16 operands at three scaling granularities (one scale
+per tensor, per token x per output channel, and the recipe's 1x128 / 128x128
+tiles) with dsmoe_fp8_gemm_granularity, and times each quantiser against the
+HBM roofline.  Its value is the recipe path's rate (both quantisations and
+the GEMM, float32 output); the error of each granularity against the float64
+product of the unquantised inputs is reported beside it, on a 256-row sample.
+
 A step is one pass of the whole hot path over one batch: dsmoe_moe_forward
 (1x128 quantisation of x, router logits, group-limited top-8 routing,
 permute, gate/up FP8 GEMM with SwiGLU and requantisation, routed and shared
@@ -44,7 +52,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="v3_prefill",
-                    choices=["v3_prefill", "v3_decode", "v3_skew", "tiny", "c2_dense"])
+                    choices=["v3_prefill", "v3_decode", "v3_skew", "tiny", "c2_dense", "c2_granularity"])
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=10)
@@ -271,6 +279,130 @@ def run_dense(args, torch):
     print(json.dumps(result), flush=True)
 
 
+def granularity_cpu_baseline(a, w, n_rows):
+    """The oracle's recipe path, as it stands: quantise the first n_rows rows
+    of A (1x128) and all of W (128x128), then the float64 product."""
+    from oracle import granularity as ogr
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    t0 = time.perf_counter()
+    ah, wh = ogr.dequantised(a[:n_rows], w, "block")
+    ah @ wh.T
+    dt = time.perf_counter() - t0
+    flops = 2.0 * n_rows * w.shape[0] * w.shape[1]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"the first {n_rows} rows of A through the oracle's block-granularity path "
+                      f"(quantisation of the A rows and all of W included; float64 NumPy), {dt:.1f} s"}
+
+
+def run_granularity(args, torch):
+    import numpy as np
+    import fp8_block_scaled_dsmoe_amd as d
+    import dsmoe_inputs as dsi
+    M, N, K = 4096, 4096, 7168
+    log(f"workload c2_granularity: M={M} N={N} K={K}, 1% x50 outliers in A, c float32")
+    a, w = dsi.dense_gemm_inputs_host(M, N, K, seed=0)
+    a_dev = torch.from_numpy(a).to("cuda").to(torch.bfloat16)
+    w_dev = torch.from_numpy(w).to("cuda").to(torch.bfloat16)
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty((d.gemm_granularity_workspace_bytes(M, N, K),), dtype=torch.uint8, device="cuda")
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa_t = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    sa_r = torch.empty((M,), dtype=torch.float32, device="cuda")
+    s1 = torch.empty((1,), dtype=torch.float32, device="cuda")
+    am = torch.empty((d.QUANT_TENSOR_SCRATCH_FLOATS,), dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps=1):
+        """Median over the steps of (event time around `reps` back-to-back calls) / reps."""
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / reps)
+        return statistics.median(ts)
+
+    flops = 2.0 * M * N * K
+    rows = np.arange(256)
+    exact = a[rows].astype(np.float64) @ w.astype(np.float64).T
+    d_norm = np.abs(a[rows]).astype(np.float64) @ np.abs(w).astype(np.float64).T
+    grans = {}
+    for g in ("tensor", "channel", "block"):
+        ms = timed(lambda: d.fp8_gemm_granularity(a_dev, w_dev, g, c=c, workspace=ws))
+        d.fp8_gemm_granularity(a_dev, w_dev, g, c=c, workspace=ws)
+        cs = c[:256].cpu().numpy().astype(np.float64)
+        grans[g] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                    "rel_frobenius": float(np.linalg.norm(cs - exact) / np.linalg.norm(exact)),
+                    "max_norm_err": float((np.abs(cs - exact) / d_norm).max())}
+        log(f"{g:8s} {ms * 1e3:8.1f} us end to end ({grans[g]['tflops']:.0f} TFLOP/s), "
+            f"rel. Frobenius error {grans[g]['rel_frobenius']:.4f}, max normalised {grans[g]['max_norm_err']:.4f}")
+
+    # the quantisers on A alone, 10 launches per timed interval (a single ~20 us
+    # launch would carry the launch latency): algorithmic bytes = 2 (bf16 read)
+    # + 1 (code) per element + scales
+    elems = M * K
+    quants = {
+        "quant_act_1x128": (lambda: d.quant_act_1x128(a_dev, qa, sa_t), 3 * elems + 4 * elems // 128),
+        "quant_rows": (lambda: d.quant_rows(a_dev, qa, sa_r), 3 * elems + 4 * M),
+        "quant_tensor": (lambda: d.quant_tensor(a_dev, qa, s1, am), 3 * elems + 8),
+    }
+    qres = {}
+    for name, (fn, nbytes) in quants.items():
+        ms = timed(fn, reps=10)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        qres[name] = {"ms": round(ms, 4), "algorithmic_bytes": nbytes, "gbps": round(gbps, 1),
+                      "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+        log(f"{name:16s} {ms * 1e3:7.1f} us, {gbps:.0f} GB/s of algorithmic bytes "
+            f"({gbps / PEAK_HBM_GBPS:.0%} of HBM peak)")
+    qres["quant_tensor"]["note"] = "two passes over x (amax, then codes): 5 B per element moved, 3 counted"
+
+    # the dominant kernel: the GEMM of the recipe path (float32 output), alone
+    d.fp8_gemm_granularity(a_dev, w_dev, "block", c=c, workspace=ws)
+    qa_b, sa_b = d.quant_act_1x128(a_dev)
+    qw_b, sw_b = d.quant_w_128x128(w_dev)
+    offsets = torch.tensor([0, M], dtype=torch.int32, device="cuda")
+    gemm_ms = timed(lambda: d.fp8_grouped_gemm(qa_b, sa_b, offsets, qw_b.unsqueeze(0), sw_b.unsqueeze(0), c=c))
+    tf_gemm = flops / (gemm_ms * 1e-3) / 1e12
+    log(f"GEMM alone {gemm_ms * 1e3:.1f} us ({tf_gemm:.0f} TFLOP/s)")
+    val = grans["block"]["tflops"]
+    result = {
+        "metric": METRIC,
+        "value": val,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": grans["block"]["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"c2_granularity: quantise A [{M}][{K}] and W [{N}][{K}] from bf16 and run "
+                               f"the FP8 GEMM, at per-tensor, per-token x per-channel and 1x128 / 128x128 "
+                               f"scaling, c float32",
+                   "M": M, "N": N, "K": K},
+        "roofline": {"bound": "mfma", "achieved": round(tf_gemm, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf_gemm / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "kernel": "dense block-scaled FP8 GEMM (256 x 256 tiles), float32 output",
+                     "algorithmic_flops": flops, "avg_ms": round(gemm_ms, 4)},
+        "granularities": grans,
+        "quantisers_on_A": qres,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = granularity_cpu_baseline(a, w, M)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -283,6 +415,9 @@ def main():
         return
     if args.workload == "c2_dense":
         run_dense(args, torch)
+        return
+    if args.workload == "c2_granularity":
+        run_granularity(args, torch)
         return
     import fp8_block_scaled_dsmoe_amd as d
     import dsmoe_inputs as dsi

@@ -22,7 +22,8 @@ __all__ = [
     "DsmoeError", "MoEDesc", "MoEWeights", "LIB_PATH", "lib",
     "quant_act_1x128", "quant_w_128x128", "route", "fp8_grouped_gemm",
     "moe_workspace_bytes", "moe_forward", "update_bias", "quantize_layer_weights",
-    "BF16", "F32",
+    "quant_rows", "quant_tensor", "gemm_granularity_workspace_bytes", "fp8_gemm_granularity",
+    "GRANULARITIES", "BF16", "F32",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsmoe.so")
@@ -30,7 +31,7 @@ BF16, F32 = 0, 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m fp8_block_scaled_dsmoe_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python fp8_block_scaled_dsmoe_amd/build.py` "
         "(hipcc, gfx950). There is no non-HIP fallback.")
 
 lib = ctypes.CDLL(LIB_PATH)
@@ -77,10 +78,22 @@ lib.dsmoe_moe_forward.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Weights
                                   _int, _vp, _vp, _sz, ctypes.POINTER(_Debug), _vp]
 lib.dsmoe_update_bias.restype = _int
 lib.dsmoe_update_bias.argtypes = [_vp, _vp, _i32, _i64, _i32, ctypes.c_float, _vp]
+lib.dsmoe_quant_rows.restype = _int
+lib.dsmoe_quant_rows.argtypes = [_vp, _int, _i64, _i64, _vp, _vp, _vp]
+lib.dsmoe_quant_tensor.restype = _int
+lib.dsmoe_quant_tensor.argtypes = [_vp, _int, _i64, _vp, _vp, _vp, _vp]
+lib.dsmoe_gemm_granularity_workspace_bytes.restype = _sz
+lib.dsmoe_gemm_granularity_workspace_bytes.argtypes = [_i64, _i64, _i64]
+lib.dsmoe_fp8_gemm_granularity.restype = _int
+lib.dsmoe_fp8_gemm_granularity.argtypes = [_vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _sz, _vp]
 
 EXPORTED = ("dsmoe_status_str", "dsmoe_abi_version", "dsmoe_quant_act_1x128", "dsmoe_quant_w_128x128",
             "dsmoe_route", "dsmoe_fp8_grouped_gemm", "dsmoe_moe_workspace_bytes", "dsmoe_moe_forward",
-            "dsmoe_update_bias")
+            "dsmoe_update_bias", "dsmoe_quant_rows", "dsmoe_quant_tensor",
+            "dsmoe_gemm_granularity_workspace_bytes", "dsmoe_fp8_gemm_granularity")
+
+# dsmoe_granularity codes
+GRANULARITIES = {"tensor": 0, "channel": 1, "block": 2}
 
 
 class DsmoeError(RuntimeError):
@@ -215,6 +228,80 @@ def fp8_grouped_gemm(a: torch.Tensor, a_scale: torch.Tensor, offsets: torch.Tens
     _check(lib.dsmoe_fp8_grouped_gemm(_p(a), _p(a_scale), _p(a_rows), _p(offsets), g, m_total, _p(w),
                                       _p(w_scale), n, k, _p(c), _dtype_code(c.dtype), _stream()),
            "dsmoe_fp8_grouped_gemm")
+    return c
+
+
+def quant_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+               scale: Optional[torch.Tensor] = None):
+    """x [rows][cols] bf16/f32 -> (q uint8 [rows][cols], scale f32 [rows]): one
+    scale per row over the whole row (see dsmoe_quant_rows)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    _dev(x, x.dtype, "x")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
+    scale = torch.empty((rows,), dtype=torch.float32, device=x.device) if scale is None else scale
+    _dev(q, torch.uint8, "q")
+    _dev(scale, torch.float32, "scale")
+    _check(lib.dsmoe_quant_rows(_p(x), _dtype_code(x.dtype), rows, cols, _p(q), _p(scale), _stream()),
+           "dsmoe_quant_rows")
+    return q, scale
+
+
+QUANT_TENSOR_SCRATCH_FLOATS = 2048
+
+
+def quant_tensor(x: torch.Tensor, q: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
+                 scratch: Optional[torch.Tensor] = None):
+    """x (any shape) bf16/f32 -> (q uint8 same shape, scale f32 [1], amax f32 [1]):
+    one scale for the whole tensor (see dsmoe_quant_tensor).  scratch: f32
+    [QUANT_TENSOR_SCRATCH_FLOATS]; the returned amax is a view of its first
+    element."""
+    _dev(x, x.dtype, "x")
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if q is None else q
+    scale = torch.empty((1,), dtype=torch.float32, device=x.device) if scale is None else scale
+    if scratch is None:
+        scratch = torch.empty((QUANT_TENSOR_SCRATCH_FLOATS,), dtype=torch.float32, device=x.device)
+    _dev(q, torch.uint8, "q")
+    _dev(scale, torch.float32, "scale")
+    _dev(scratch, torch.float32, "scratch")
+    if q.numel() != x.numel():
+        raise ValueError("q must have as many elements as x")
+    if scratch.numel() < QUANT_TENSOR_SCRATCH_FLOATS:
+        raise ValueError(f"scratch must hold {QUANT_TENSOR_SCRATCH_FLOATS} floats")
+    _check(lib.dsmoe_quant_tensor(_p(x), _dtype_code(x.dtype), x.numel(), _p(q), _p(scale), _p(scratch),
+                                  _stream()), "dsmoe_quant_tensor")
+    return q, scale, scratch[:1]
+
+
+def gemm_granularity_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(lib.dsmoe_gemm_granularity_workspace_bytes(m, n, k))
+
+
+def fp8_gemm_granularity(a: torch.Tensor, w: torch.Tensor, granularity: str,
+                         c: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """c f32 [M][N] = A W^T with A [M][K] and W [N][K] (bf16 or f32, same
+    dtype) quantised to E4M3 at `granularity` ("tensor", "channel" or
+    "block"); see dsmoe_fp8_gemm_granularity."""
+    if granularity not in GRANULARITIES:
+        raise ValueError(f"granularity must be one of {tuple(GRANULARITIES)}")
+    if a.dim() != 2 or w.dim() != 2:
+        raise ValueError("a and w must be 2-D")
+    _dev(a, a.dtype, "a")
+    _dev(w, a.dtype, "w")
+    m, k = a.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("a and w must have the same K")
+    c = torch.empty((m, n), dtype=torch.float32, device=a.device) if c is None else c
+    _dev(c, torch.float32, "c")
+    need = gemm_granularity_workspace_bytes(m, n, k)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=a.device)
+    _dev(workspace, torch.uint8, "workspace")
+    _check(lib.dsmoe_fp8_gemm_granularity(_p(a), _p(w), _dtype_code(a.dtype), m, n, k,
+                                          GRANULARITIES[granularity], _p(c), _p(workspace),
+                                          workspace.numel(), _stream()), "dsmoe_fp8_gemm_granularity")
     return c
 
 

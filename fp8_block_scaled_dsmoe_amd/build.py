@@ -1,6 +1,6 @@
 """Build libdsmoe.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-    python -m fp8_block_scaled_dsmoe_amd.build
+    python fp8_block_scaled_dsmoe_amd/build.py
 
 Every source is compiled on each call (no staleness checks), in parallel,
 then linked into fp8_block_scaled_dsmoe_amd/libdsmoe.so next to this file.
@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsmoe.so")
-SOURCES = ["abi.hip", "quant.hip", "route.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "quant.hip", "granularity.hip", "route.hip", "gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -96,6 +96,45 @@ dsmoe_status check_desc(const dsmoe_moe_desc* d, int64_t T) {
   return DSMOE_OK;
 }
 
+// Workspace layout of dsmoe_fp8_gemm_granularity (every region 256-byte
+// aligned): codes and the 1x128 / 128x128 scale layouts of both operands,
+// the per-row scales, the per-tensor scale and amax slots, the offsets {0, M}.
+struct GranLayout {
+  size_t qa, qw, sa, sw, row_a, row_w, scales, amax_a, amax_w, offsets, total;
+};
+
+GranLayout gran_layout(int64_t M, int64_t N, int64_t K) {
+  // the header's scratch size must cover the kernels' slots
+  static_assert(DSMOE_QUANT_TENSOR_SCRATCH_FLOATS >= 64 * 32, "amax scratch");
+  GranLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  L.qa = take(static_cast<size_t>(M) * K);
+  L.qw = take(static_cast<size_t>(N) * K);
+  L.sa = take(static_cast<size_t>(M) * (K / 128) * 4);
+  L.sw = take(static_cast<size_t>(N / 128) * (K / 128) * 4);
+  L.row_a = take(static_cast<size_t>(M) * 4);
+  L.row_w = take(static_cast<size_t>(N) * 4);
+  L.scales = take(2 * 4);  // per-tensor scale of A, of W
+  L.amax_a = take(DSMOE_QUANT_TENSOR_SCRATCH_FLOATS * 4);
+  L.amax_w = take(DSMOE_QUANT_TENSOR_SCRATCH_FLOATS * 4);
+  L.offsets = take(2 * 4);
+  L.total = off;
+  return L;
+}
+
+dsmoe_status check_gran_shape(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N <= 0 || K <= 0 || N % 128 || K % 128 || K > kMaxK) return DSMOE_ERR_SHAPE;
+  if (M > kI32Max || N > kI32Max) return DSMOE_ERR_SHAPE;
+  if (M * K > (1LL << 40) || N * K > (1LL << 40)) return DSMOE_ERR_SHAPE;
+  if (((M + 15) / 16 + 1) * (N / 128) >= kI32Max) return DSMOE_ERR_SHAPE;
+  return DSMOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -384,6 +423,116 @@ dsmoe_status dsmoe_update_bias(float* bias, const int32_t* counts, int32_t E, in
   if (s != DSMOE_OK) return s;
   return launch_status(dsmoe::launch_update_bias(bias, counts, E, T, K, gamma,
                                                  static_cast<hipStream_t>(stream)));
+}
+
+dsmoe_status dsmoe_quant_rows(const void* x, int xt, int64_t rows, int64_t cols, uint8_t* q,
+                              float* scale, void* stream) {
+  if (!valid_dtype(xt)) return DSMOE_ERR_DTYPE;
+  if (rows < 0 || cols < 8 || cols % 8 || cols > dsmoe::quant_rows_max_cols()) return DSMOE_ERR_SHAPE;
+  if (rows > kI32Max) return DSMOE_ERR_SHAPE;
+  if (rows == 0) return DSMOE_OK;
+  if (!x || !q || !scale) return DSMOE_ERR_NULL;
+  // rows of 8 elements keep every row start 16-byte aligned for bf16; f32 needs 32 bytes
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scale, 4)) return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  return launch_status(dsmoe::launch_quant_rows(x, xt == DSMOE_F32, rows, cols, q, scale,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+dsmoe_status dsmoe_quant_tensor(const void* x, int xt, int64_t n, uint8_t* q, float* scale,
+                                float* amax, void* stream) {
+  if (!valid_dtype(xt)) return DSMOE_ERR_DTYPE;
+  if (n < 0 || n % 8 || n > (1LL << 40)) return DSMOE_ERR_SHAPE;
+  if (!scale || !amax) return DSMOE_ERR_NULL;
+  if (n > 0 && (!x || !q)) return DSMOE_ERR_NULL;
+  if ((x && !aligned(x, 16)) || (q && !aligned(q, 8)) || !aligned(scale, 4) || !aligned(amax, 4))
+    return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  return launch_status(dsmoe::launch_quant_tensor(x, xt == DSMOE_F32, n, q, scale, amax,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+size_t dsmoe_gemm_granularity_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (check_gran_shape(M, N, K) != DSMOE_OK) return 0;
+  return gran_layout(M, N, K).total;
+}
+
+dsmoe_status dsmoe_fp8_gemm_granularity(const void* a, const void* w, int t, int64_t M, int64_t N,
+                                        int64_t K, int granularity, float* c, void* workspace,
+                                        size_t ws_bytes, void* stream) {
+  if (!valid_dtype(t)) return DSMOE_ERR_DTYPE;
+  if (granularity != DSMOE_SCALE_TENSOR && granularity != DSMOE_SCALE_CHANNEL &&
+      granularity != DSMOE_SCALE_BLOCK)
+    return DSMOE_ERR_SHAPE;
+  dsmoe_status s = check_gran_shape(M, N, K);
+  if (s != DSMOE_OK) return s;
+  if (M == 0) return DSMOE_OK;
+  if (!a || !w || !c) return DSMOE_ERR_NULL;
+  const GranLayout L = gran_layout(M, N, K);
+  if (!workspace || ws_bytes < L.total) return DSMOE_ERR_WORKSPACE;
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(c, 16) || !aligned(workspace, 256))
+    return DSMOE_ERR_ALIGN;
+  s = check_device();
+  if (s != DSMOE_OK) return s;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool f32 = t == DSMOE_F32;
+  char* ws = static_cast<char*>(workspace);
+  uint8_t* qa = reinterpret_cast<uint8_t*>(ws + L.qa);
+  uint8_t* qw = reinterpret_cast<uint8_t*>(ws + L.qw);
+  float* sa = reinterpret_cast<float*>(ws + L.sa);
+  float* sw = reinterpret_cast<float*>(ws + L.sw);
+  float* row_a = reinterpret_cast<float*>(ws + L.row_a);
+  float* row_w = reinterpret_cast<float*>(ws + L.row_w);
+  float* scales = reinterpret_cast<float*>(ws + L.scales);
+  float* amax_a = reinterpret_cast<float*>(ws + L.amax_a);
+  float* amax_w = reinterpret_cast<float*>(ws + L.amax_w);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  const int64_t kt = K / 128, nb = N / 128;
+#define DSMOE_TRY(expr)                          \
+  do {                                           \
+    if ((expr) != hipSuccess) return DSMOE_ERR_LAUNCH; \
+  } while (0)
+  switch (granularity) {
+    case DSMOE_SCALE_BLOCK:
+      DSMOE_TRY(dsmoe::launch_quant_act(a, f32, M, K, qa, sa, st));
+      DSMOE_TRY(dsmoe::launch_quant_w(w, f32, 1, N, K, qw, sw, st));
+      break;
+    case DSMOE_SCALE_CHANNEL:
+      DSMOE_TRY(dsmoe::launch_quant_rows(a, f32, M, K, qa, row_a, st));
+      DSMOE_TRY(dsmoe::launch_quant_rows(w, f32, N, K, qw, row_w, st));
+      DSMOE_TRY(dsmoe::launch_broadcast_scale(sa, M, kt, row_a, 1, st));
+      DSMOE_TRY(dsmoe::launch_broadcast_scale(sw, nb, kt, nullptr, 0, st));
+      break;
+    default:  // DSMOE_SCALE_TENSOR
+      DSMOE_TRY(dsmoe::launch_quant_tensor(a, f32, M * K, qa, scales + 0, amax_a, st));
+      DSMOE_TRY(dsmoe::launch_quant_tensor(w, f32, N * K, qw, scales + 1, amax_w, st));
+      DSMOE_TRY(dsmoe::launch_broadcast_scale(sa, M, kt, scales + 0, 0, st));
+      DSMOE_TRY(dsmoe::launch_broadcast_scale(sw, nb, kt, scales + 1, 0, st));
+      break;
+  }
+  DSMOE_TRY(dsmoe::launch_prep_offsets(offsets, static_cast<int32_t>(M), st));
+  dsmoe::GemmProblem p{};
+  p.a = qa;
+  p.a_scale = sa;
+  p.offsets = offsets;
+  p.G = 1;
+  p.M_total = M;
+  p.w = qw;
+  p.w_scale = sw;
+  p.N = N;
+  p.K = K;
+  p.c = c;
+  p.c_f32 = true;
+  p.epi = dsmoe::Epilogue::kStore;
+  p.row_limit = M;
+  p.rows_hint = M;
+  DSMOE_TRY(dsmoe::launch_grouped_gemm(p, st));
+  if (granularity == DSMOE_SCALE_CHANNEL) DSMOE_TRY(dsmoe::launch_scale_cols(c, M, N, row_w, st));
+#undef DSMOE_TRY
+  return DSMOE_OK;
 }
 
 }  // extern "C"

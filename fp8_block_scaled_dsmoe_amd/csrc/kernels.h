@@ -14,6 +14,23 @@ hipError_t launch_quant_act(const void* x, bool x_f32, int64_t rows, int64_t col
 hipError_t launch_quant_w(const void* w, bool w_f32, int64_t n_mats, int64_t n, int64_t k,
                           uint8_t* q, float* scale, hipStream_t s);
 
+// granularity.hip
+int64_t quant_rows_max_cols();
+// one scale per row over the whole row; cols % 8 == 0, cols <= quant_rows_max_cols()
+hipError_t launch_quant_rows(const void* x, bool x_f32, int64_t rows, int64_t cols, uint8_t* q,
+                             float* scale, hipStream_t s);
+// one scale for n elements (n % 8 == 0); amax_scratch holds
+// quant_tensor_scratch_floats() floats, max |x| in element 0 afterwards
+int64_t quant_tensor_scratch_floats();
+hipError_t launch_quant_tensor(const void* x, bool x_f32, int64_t n, uint8_t* q, float* scale,
+                               float* amax_scratch, hipStream_t s);
+hipError_t launch_prep_offsets(int32_t* offsets, int32_t m, hipStream_t s);
+// dst[r][t] = src ? src[r * src_stride] : 1 for r < rows, t < tiles
+hipError_t launch_broadcast_scale(float* dst, int64_t rows, int64_t tiles, const float* src,
+                                  int64_t src_stride, hipStream_t s);
+// c[m][n] *= col[n], float32 c [M][N], N % 4 == 0
+hipError_t launch_scale_cols(float* c, int64_t m, int64_t n, const float* col, hipStream_t s);
+
 // route.hip
 // H is split over router_splits() blocks for small T; the splits' partial
 // sums go to `partial` (router_partial_bytes(), NULL when that is 0)

@@ -276,6 +276,82 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
 dsmoe_status dsmoe_update_bias(float* bias, const int32_t* counts, int32_t E, int64_t T,
                                int32_t K, float gamma, void* stream);
 
+/*
+ * Coarser scaling granularities, for comparison with the recipe's 1x128 /
+ * 128x128 tiles.  Source: infra answer, FP8 paragraph (per-tensor E4M3
+ * scaling lets a single outlier stretch the scale of a whole tensor and so
+ * the quantisation error of everything else; the fine-grained tiles are the
+ * recipe's answer; per-token x per-channel scaling, which needs no tiling, is
+ * named there as not discussed); V3 notes §6.1 (the recipe itself).
+ * Every scale below follows the rule of dsmoe_quant_act_1x128 (s =
+ * fl32(amax / 448), s = 1 when amax = 0, q = E4M3(fl32(x / s))), taken over
+ * a different set of values.
+ */
+
+/*
+ * dsmoe_quant_rows -- one scale per row, over the whole row: per token for
+ * an activation [tokens][channels], per output channel for a weight [N][K].
+ *
+ *   x      [rows][cols] row-major, dtype xt (DSMOE_BF16 or DSMOE_F32)
+ *   q      [rows][cols] uint8 E4M3FN codes (output)
+ *   scale  [rows] float32 (output)
+ * Requires rows >= 0, 8 <= cols <= 32768, cols % 8 == 0.
+ */
+dsmoe_status dsmoe_quant_rows(const void* x, int xt, int64_t rows, int64_t cols, uint8_t* q,
+                              float* scale, void* stream);
+
+/* Floats of the scratch buffer dsmoe_quant_tensor takes (8 KB). */
+#define DSMOE_QUANT_TENSOR_SCRATCH_FLOATS 2048
+
+/*
+ * dsmoe_quant_tensor -- one scale for a whole tensor of n elements.
+ *
+ *   x      [n] dtype xt (any shape, contiguous)
+ *   q      [n] uint8 E4M3FN codes (output)
+ *   scale  [1] float32 (output)
+ *   amax   [DSMOE_QUANT_TENSOR_SCRATCH_FLOATS] float32 scratch: the first
+ *          pass merges the blocks' maxima into 64 slots on separate 128-byte
+ *          lines of it; on return amax[0] = max |x| (the rest is
+ *          unspecified).  Must not alias x, q or scale.
+ * Three kernels on `stream`: clear the slots, amax pass (exact, independent
+ * of order), encode pass.  n = 0 writes amax[0] = 0 and scale = 1.
+ * Requires n >= 0, n % 8 == 0.
+ */
+dsmoe_status dsmoe_quant_tensor(const void* x, int xt, int64_t n, uint8_t* q, float* scale,
+                                float* amax, void* stream);
+
+typedef enum dsmoe_granularity {
+  DSMOE_SCALE_TENSOR = 0,  /* one scale for A, one for W */
+  DSMOE_SCALE_CHANNEL = 1, /* one per row of A (token), one per row of W (output channel) */
+  DSMOE_SCALE_BLOCK = 2    /* 1x128 tiles of A, 128x128 blocks of W (the recipe) */
+} dsmoe_granularity;
+
+/* Workspace of dsmoe_fp8_gemm_granularity (0 for invalid sizes). */
+size_t dsmoe_gemm_granularity_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * dsmoe_fp8_gemm_granularity -- c = A W^T with both operands quantised to
+ * E4M3 at one granularity, on the device from the high-precision inputs.
+ *
+ *   a          [M][K] dtype t (DSMOE_BF16 or DSMOE_F32)
+ *   w          [N][K] dtype t
+ *   c          [M][N] float32 (output)
+ *   workspace  device buffer of at least
+ *              dsmoe_gemm_granularity_workspace_bytes(M, N, K), 256-byte
+ *              aligned; holds the codes and scales of both operands after
+ *              the call (layout private)
+ * TENSOR and CHANNEL quantise with dsmoe_quant_tensor / dsmoe_quant_rows and
+ * broadcast the scales into the 1x128 / 128x128 layouts of
+ * dsmoe_fp8_grouped_gemm; a per-output-channel scale of W is applied to c
+ * after the GEMM (c[m][n] = fl32(sum * sw[n])).  BLOCK is the recipe
+ * (dsmoe_quant_act_1x128, dsmoe_quant_w_128x128).  The GEMM promotes every
+ * 128-K chunk to float32 as in dsmoe_fp8_grouped_gemm.
+ * Requires M >= 0, N and K positive multiples of 128, K <= 32768.
+ */
+dsmoe_status dsmoe_fp8_gemm_granularity(const void* a, const void* w, int t, int64_t M, int64_t N,
+                                        int64_t K, int granularity, float* c, void* workspace,
+                                        size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ def _declared():
 def test_library_exports_every_declared_function():
     import fp8_block_scaled_dsmoe_amd as d
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(d.lib, n), f"{n} not exported"
     assert sorted(d.EXPORTED) == names
@@ -70,6 +70,40 @@ def test_quant_validation_errors():
     assert L.dsmoe_quant_w_128x128(_vp(ALIGNED), 0, 1, 130, 128, _vp(ALIGNED), _vp(ALIGNED), None) == 2
     assert L.dsmoe_quant_w_128x128(_vp(ALIGNED), 0, 1, 128, 128, None, _vp(ALIGNED), None) == 1
     assert L.dsmoe_quant_w_128x128(_vp(ALIGNED), 0, 1, 128, 128, _vp(ALIGNED), _vp(MISALIGNED), None) == 3
+
+
+def test_granularity_validation_errors():
+    import fp8_block_scaled_dsmoe_amd as d
+    L = d.lib
+    a = _vp(ALIGNED)
+    # per-row: cols a multiple of 8, at most 32768
+    assert L.dsmoe_quant_rows(a, 0, 4, 100, a, a, None) == 2
+    assert L.dsmoe_quant_rows(a, 0, 4, 32768 + 8, a, a, None) == 2
+    assert L.dsmoe_quant_rows(a, 0, 4, 0, a, a, None) == 2
+    assert L.dsmoe_quant_rows(a, 3, 4, 128, a, a, None) == 4
+    assert L.dsmoe_quant_rows(a, 0, 4, 128, a, None, None) == 1
+    assert L.dsmoe_quant_rows(_vp(MISALIGNED), 0, 4, 128, a, a, None) == 3
+    assert L.dsmoe_quant_rows(None, 0, 0, 128, None, None, None) == 0          # empty: no-op
+    # per-tensor: n a multiple of 8; scale and amax always required
+    assert L.dsmoe_quant_tensor(a, 0, 12, a, a, a, None) == 2
+    assert L.dsmoe_quant_tensor(a, 0, -8, a, a, a, None) == 2
+    assert L.dsmoe_quant_tensor(a, 0, 16, a, a, None, None) == 1
+    assert L.dsmoe_quant_tensor(None, 0, 16, a, a, a, None) == 1
+    assert L.dsmoe_quant_tensor(a, 0, 16, a, a, _vp(MISALIGNED), None) == 3
+    # GEMM at a granularity
+    G = L.dsmoe_fp8_gemm_granularity
+    ws = d.gemm_granularity_workspace_bytes(64, 256, 512)
+    assert ws >= 64 * 512 + 256 * 512 + 64 * 4 * 4 + 2 * 4 * 4
+    assert d.gemm_granularity_workspace_bytes(64, 200, 512) == 0
+    assert d.gemm_granularity_workspace_bytes(64, 256, 32768 + 128) == 0
+    assert G(a, a, 0, 64, 256, 512, 3, a, a, ws, None) == 2                     # unknown granularity
+    assert G(a, a, 2, 64, 256, 512, 0, a, a, ws, None) == 4
+    assert G(a, a, 0, 64, 200, 512, 0, a, a, ws, None) == 2
+    assert G(a, a, 0, 64, 256, 512, 0, a, a, ws - 1, None) == 5
+    assert G(a, a, 0, 64, 256, 512, 0, a, None, ws, None) == 5
+    assert G(a, None, 0, 64, 256, 512, 0, a, a, ws, None) == 1
+    assert G(a, a, 0, 64, 256, 512, 0, a, _vp(ALIGNED + 16), ws, None) == 3    # workspace 256-aligned
+    assert G(None, None, 0, 0, 256, 512, 1, None, None, 0, None) == 0          # M = 0: no-op
 
 
 def test_route_and_bias_validation_errors():
