@@ -8,6 +8,13 @@ seeded recipe with 1% x50 outliers in A, quantised 1x128 / 128x128 on the
 GPU, then dsmoe_fp8_grouped_gemm with one group, timed with its inputs warm
 in the 256 MB MALL and with a 512 MB write between launches that evicts them.
 
+The decode-serving workload (--workload v3_decode_serving) runs the V3
+decode batch (T=64) through dsmoe_moe_forward_serving: the shared expert as a
+9th routed expert and --extra-slots copies of hot experts (default 64: 256 +
+64 slots), planned from the loads of one plain forward on the batch and
+placed once before timing.  A step is the serving forward plus the bias
+update; the plain decode step is timed in the same process for comparison.
+
 The granularity workload (--workload c2_granularity) runs the same GEMM
 end to end from the bf16 operands at three scaling granularities (one scale
 per tensor, per token x per output channel, and the recipe's 1x128 / 128x128
@@ -52,7 +59,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="v3_prefill",
-                    choices=["v3_prefill", "v3_decode", "v3_skew", "tiny", "c2_dense", "c2_granularity"])
+                    choices=["v3_prefill", "v3_decode", "v3_skew", "tiny", "c2_dense", "c2_granularity",
+                             "v3_decode_serving"])
+    ap.add_argument("--extra-slots", type=int, default=64,
+                    help="v3_decode_serving: copies of hot experts beyond one slot per expert")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=10)
@@ -403,6 +413,158 @@ def run_granularity(args, torch):
     print(json.dumps(result), flush=True)
 
 
+def run_serving(args, torch):
+    import numpy as np
+    import fp8_block_scaled_dsmoe_amd as d
+    import dsmoe_inputs as dsi
+    cfg = dsi.LAYER_CONFIGS["v3_decode"]
+    out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+    T, H, I, E, K = cfg.T, cfg.H, cfg.I, cfg.E, cfg.K
+    R = args.extra_slots
+    S = E + R
+    log(f"workload v3_decode_serving: T={T} H={H} E={E} G={cfg.G} Mg={cfg.Mg} K={K} I={I}, "
+        f"{R} extra slots, shared expert as a routed group")
+    x, bias, weights, quant_w_ms = build_layer(cfg, d, torch, dsi)
+    desc = d.MoEDesc(H, I, E, cfg.G, cfg.Mg, K, 1)
+    y = torch.empty((T, H), dtype=out_dtype, device="cuda")
+    counts = torch.empty((E,), dtype=torch.int32, device="cuda")
+    ws_plain = torch.empty((d.moe_workspace_bytes(desc, T),), dtype=torch.uint8, device="cuda")
+    ws_srv = torch.empty((d.moe_serving_workspace_bytes(desc, T, S),), dtype=torch.uint8, device="cuda")
+    bias0 = bias.clone()
+
+    # observed loads: one plain forward on the batch (the bias is not updated)
+    d.moe_forward(desc, weights, bias, x, y=y, counts=counts, workspace=ws_plain)
+    observed = counts.clone()
+
+    def once(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        out = fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return out, e0.elapsed_time(e1)
+
+    (slot_first, slot_expert), _ = once(lambda: d.plan_replicas(observed, R))      # warm
+    (slot_first, slot_expert), plan_ms = once(lambda: d.plan_replicas(observed, R))
+    slot_w, place_ms = once(lambda: d.place_layer_replicas(weights, slot_expert))
+    place_bytes = 2 * S * (3 * H * I + ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128)) * 4)
+
+    def timed_steps(step, n_ev):
+        for _ in range(args.warmup):
+            step(None)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+        for row in ev:
+            for e in row:
+                e.record()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(args.steps):
+            step(ev[i])
+        t1.record()
+        torch.cuda.synchronize()
+        stages = [statistics.mean(r[j].elapsed_time(r[j + 1]) for r in ev) for j in range(n_ev - 1)]
+        return t0.elapsed_time(t1) / args.steps, stages
+
+    def plain(ev):
+        d.moe_forward(desc, weights, bias, x, y=y, counts=counts, workspace=ws_plain,
+                      stage_events=None if ev is None else [e.cuda_event for e in ev])
+        d.update_bias(bias, counts, T, K, 0.001)
+
+    def serving(ev):
+        d.moe_forward_serving(desc, slot_w, slot_first, slot_expert, bias, x, y=y, counts=counts,
+                              workspace=ws_srv, stage_events=None if ev is None else [e.cuda_event for e in ev])
+        d.update_bias(bias, counts, T, K, 0.001)
+
+    # no extra slots: only the shared expert joins the routed launches
+    sf0, se0 = d.plan_replicas(observed, 0)
+    slot_w0 = d.place_layer_replicas(weights, se0)
+    ws0 = torch.empty((d.moe_serving_workspace_bytes(desc, T, E),), dtype=torch.uint8, device="cuda")
+
+    def serving0(ev):
+        d.moe_forward_serving(desc, slot_w0, sf0, se0, bias, x, y=y, counts=counts, workspace=ws0,
+                              stage_events=None if ev is None else [e.cuda_event for e in ev])
+        d.update_bias(bias, counts, T, K, 0.001)
+
+    plain_ms, plain_st = timed_steps(plain, d.STAGE_EVENTS)
+    bias.copy_(bias0)
+    srv0_ms, srv0_st = timed_steps(serving0, d.SERVING_STAGE_EVENTS)
+    del slot_w0
+    torch.cuda.empty_cache()
+    bias.copy_(bias0)
+    srv_ms, srv_st = timed_steps(serving, d.SERVING_STAGE_EVENTS)
+    srv_stage = dict(zip(d.SERVING_STAGES, srv_st))
+    plain_stage = dict(zip(d.STAGES, plain_st))
+    log(f"plain decode {plain_ms:.3f} ms/step; serving without copies {srv0_ms:.3f}; "
+        f"serving {srv_ms:.3f} ms/step; serving stages " +
+        ", ".join(f"{k} {v:.3f}" for k, v in srv_stage.items()))
+
+    # loads of the last step over the plan's slots
+    c_last = counts.cpu().numpy()
+    off = torch.tensor(np.concatenate([[0], np.cumsum(c_last)]), dtype=torch.int32, device="cuda")
+    phys = d.slot_offsets(off, slot_first, slot_expert, T).cpu().numpy()
+    rows_slot = np.diff(phys[:S + 1])
+    active = int(np.count_nonzero(rows_slot))
+    obs = observed.cpu().numpy()
+    n_rep = np.diff(slot_first.cpu().numpy())
+    rows1 = T * K + T
+    g1_bytes = ((active + 1) * 2 * I * H + (active + 1) * (2 * I // 128) * (H // 128) * 4 +
+                T * H + T * (H // 128) * 4 + rows1 * I + rows1 * (I // 128) * 4)
+    g1_ms = srv_stage["gemm1_swiglu_requant"]
+    g1_gbps = g1_bytes / (g1_ms * 1e-3) / 1e9
+    w_bytes = (active + 1) * 3 * H * I
+    layer_gbps = (w_bytes + T * H * 4 + E * H * 2) / (srv_ms * 1e-3) / 1e9
+    log(f"slots holding rows: {active} of {S}; max rows per slot {rows_slot.max()} (per expert "
+        f"{c_last.max()}); plan {plan_ms * 1e3:.1f} us, placement {place_ms:.2f} ms "
+        f"({place_bytes / (place_ms * 1e-3) / 1e9:.0f} GB/s)")
+    result = {
+        "metric": METRIC,
+        "value": round(T / (srv_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(srv_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"v3_decode_serving: DeepSeekMoE layer forward over {S} expert slots "
+                               f"({R} copies of hot experts planned from observed loads) with the shared "
+                               f"expert as a 9th routed expert, + bias update, T={T}, H={H}, E={E}, "
+                               f"top-{K} within {cfg.Mg} of {cfg.G} groups, I={I}, y {args.out_dtype}",
+                   "T": T, "H": H, "E": E, "G": cfg.G, "Mg": cfg.Mg, "K": K, "I": I, "slots": S},
+        "roofline": {"bound": "hbm", "achieved": round(g1_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(g1_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "gate/up grouped FP8 GEMM + SwiGLU + 1x128 requant over the slots (one launch)",
+                     "algorithmic_bytes": int(g1_bytes), "avg_ms": round(g1_ms, 4)},
+        "layer_hbm_gbps": round(layer_gbps, 1),
+        "layer_frac_hbm_peak": round(layer_gbps / PEAK_HBM_GBPS, 4),
+        "stage_ms": {k: round(v, 4) for k, v in srv_stage.items()},
+        "plain_decode": {"ms_per_step": round(plain_ms, 4), "tokens_per_s": round(T / (plain_ms * 1e-3), 1),
+                         "stage_ms": {k: round(v, 4) for k, v in plain_stage.items()}},
+        "serving_without_copies": {"ms_per_step": round(srv0_ms, 4),
+                                   "tokens_per_s": round(T / (srv0_ms * 1e-3), 1),
+                                   "stage_ms": {k: round(v, 4) for k, v in
+                                                zip(d.SERVING_STAGES, srv0_st)}},
+        "slots": {"total": S, "holding_rows_last_step": active,
+                  "max_rows_per_slot_last_step": int(rows_slot.max()),
+                  "max_rows_per_expert_last_step": int(c_last.max()),
+                  "planned_from_max_load": int(obs.max()),
+                  "planned_max_load_per_slot": round(float((obs / n_rep).max()), 3),
+                  "max_copies_of_one_expert": int(n_rep.max())},
+        "plan_us": round(plan_ms * 1e3, 2),
+        "placement_ms": round(place_ms, 3),
+        "placement_gbps": round(place_bytes / (place_ms * 1e-3) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens, torch, dsi)
+        result["cpu_baseline"]["sample"] += " (the serving forward computes the same layer)"
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -418,6 +580,9 @@ def main():
         return
     if args.workload == "c2_granularity":
         run_granularity(args, torch)
+        return
+    if args.workload == "v3_decode_serving":
+        run_serving(args, torch)
         return
     import fp8_block_scaled_dsmoe_amd as d
     import dsmoe_inputs as dsi

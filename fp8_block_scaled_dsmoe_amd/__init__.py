@@ -23,7 +23,8 @@ __all__ = [
     "quant_act_1x128", "quant_w_128x128", "route", "fp8_grouped_gemm",
     "moe_workspace_bytes", "moe_forward", "update_bias", "quantize_layer_weights",
     "quant_rows", "quant_tensor", "gemm_granularity_workspace_bytes", "fp8_gemm_granularity",
-    "GRANULARITIES", "BF16", "F32",
+    "GRANULARITIES", "plan_replicas", "place_replicas", "place_layer_replicas", "slot_offsets",
+    "moe_serving_workspace_bytes", "moe_forward_serving", "BF16", "F32",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsmoe.so")
@@ -86,11 +87,26 @@ lib.dsmoe_gemm_granularity_workspace_bytes.restype = _sz
 lib.dsmoe_gemm_granularity_workspace_bytes.argtypes = [_i64, _i64, _i64]
 lib.dsmoe_fp8_gemm_granularity.restype = _int
 lib.dsmoe_fp8_gemm_granularity.argtypes = [_vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _sz, _vp]
+lib.dsmoe_plan_replicas.restype = _int
+lib.dsmoe_plan_replicas.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp]
+lib.dsmoe_place_replicas.restype = _int
+lib.dsmoe_place_replicas.argtypes = [_vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp]
+lib.dsmoe_slot_offsets.restype = _int
+lib.dsmoe_slot_offsets.argtypes = [_vp, _i32, _vp, _vp, _i32, _i64, _vp, _vp]
+lib.dsmoe_moe_serving_workspace_bytes.restype = _sz
+lib.dsmoe_moe_serving_workspace_bytes.argtypes = [ctypes.POINTER(_Desc), _i64, _i32]
+lib.dsmoe_moe_forward_serving.restype = _int
+lib.dsmoe_moe_forward_serving.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Weights), _vp, _vp, _i32,
+                                          _vp, _vp, _i64, _vp, _int, _vp, _vp, _sz, ctypes.POINTER(_vp), _vp]
+SERVING_STAGE_EVENTS = 5
+SERVING_STAGES = ("quant_route_permute", "gemm1_swiglu_requant", "gemm2_routed_and_shared", "combine")
 
 EXPORTED = ("dsmoe_status_str", "dsmoe_abi_version", "dsmoe_quant_act_1x128", "dsmoe_quant_w_128x128",
             "dsmoe_route", "dsmoe_fp8_grouped_gemm", "dsmoe_moe_workspace_bytes", "dsmoe_moe_forward",
             "dsmoe_update_bias", "dsmoe_quant_rows", "dsmoe_quant_tensor",
-            "dsmoe_gemm_granularity_workspace_bytes", "dsmoe_fp8_gemm_granularity")
+            "dsmoe_gemm_granularity_workspace_bytes", "dsmoe_fp8_gemm_granularity",
+            "dsmoe_plan_replicas", "dsmoe_place_replicas", "dsmoe_slot_offsets", "dsmoe_moe_serving_workspace_bytes",
+            "dsmoe_moe_forward_serving")
 
 # dsmoe_granularity codes
 GRANULARITIES = {"tensor": 0, "channel": 1, "block": 2}
@@ -406,6 +422,100 @@ def moe_forward(desc: MoEDesc, weights: MoEWeights, bias: torch.Tensor, x: torch
                                  ctypes.byref(dbg_c) if dbg_c is not None else None, _stream()),
            "dsmoe_moe_forward")
     return y, counts, dbg
+
+
+def plan_replicas(counts: torch.Tensor, n_extra: int):
+    """counts int32 [E] (device) -> (slot_first int32 [E+1], slot_expert int32
+    [E + n_extra]) on the device (dsmoe_plan_replicas)."""
+    _dev(counts, torch.int32, "counts")
+    e = counts.numel()
+    slot_first = torch.empty((e + 1,), dtype=torch.int32, device=counts.device)
+    slot_expert = torch.empty((e + n_extra,), dtype=torch.int32, device=counts.device)
+    _check(lib.dsmoe_plan_replicas(_p(counts), e, n_extra, _p(slot_first), _p(slot_expert), _stream()),
+           "dsmoe_plan_replicas")
+    return slot_first, slot_expert
+
+
+def place_replicas(w: torch.Tensor, w_scale: torch.Tensor, slot_expert: torch.Tensor):
+    """w uint8 [E][N][K], w_scale f32 [E][N/128][K/128] -> (w_slots [S][N][K],
+    s_slots [S][N/128][K/128]) with slot s holding expert slot_expert[s]
+    (dsmoe_place_replicas)."""
+    _dev(w, torch.uint8, "w")
+    _dev(w_scale, torch.float32, "w_scale")
+    _dev(slot_expert, torch.int32, "slot_expert")
+    _, n, k = w.shape
+    S = slot_expert.numel()
+    w_slots = torch.empty((S, n, k), dtype=torch.uint8, device=w.device)
+    s_slots = torch.empty((S, n // 128, k // 128), dtype=torch.float32, device=w.device)
+    _check(lib.dsmoe_place_replicas(_p(w), _p(w_scale), n, k, _p(slot_expert), S, _p(w_slots), _p(s_slots),
+                                    _stream()), "dsmoe_place_replicas")
+    return w_slots, s_slots
+
+
+def place_layer_replicas(weights: "MoEWeights", slot_expert: torch.Tensor) -> "MoEWeights":
+    """The layer's weights with W13 and W2 laid out over the slots of a plan;
+    the shared expert and the router are shared with `weights`."""
+    w13, s13 = place_replicas(weights.w13, weights.s13, slot_expert)
+    w2, s2 = place_replicas(weights.w2, weights.s2, slot_expert)
+    return MoEWeights(w13, s13, w2, s2, weights.w13_sh, weights.s13_sh, weights.w2_sh, weights.s2_sh,
+                      weights.router_w)
+
+
+def slot_offsets(offsets: torch.Tensor, slot_first: torch.Tensor, slot_expert: torch.Tensor,
+                 extra_rows: int = -1):
+    """Group offsets of the slots of a plan (dsmoe_slot_offsets): int32
+    [S + 2], the last entry meaningful only when extra_rows >= 0."""
+    for t, n in ((offsets, "offsets"), (slot_first, "slot_first"), (slot_expert, "slot_expert")):
+        _dev(t, torch.int32, n)
+    e = offsets.numel() - 1
+    S = slot_expert.numel()
+    phys = torch.empty((S + 2,), dtype=torch.int32, device=offsets.device)
+    _check(lib.dsmoe_slot_offsets(_p(offsets), e, _p(slot_first), _p(slot_expert), S, extra_rows, _p(phys),
+                                  _stream()), "dsmoe_slot_offsets")
+    return phys
+
+
+def moe_serving_workspace_bytes(desc: "MoEDesc", T: int, n_slots: int) -> int:
+    d = desc._c()
+    return int(lib.dsmoe_moe_serving_workspace_bytes(ctypes.byref(d), T, n_slots))
+
+
+def moe_forward_serving(desc: "MoEDesc", slot_weights: "MoEWeights", slot_first: torch.Tensor,
+                        slot_expert: torch.Tensor, bias: torch.Tensor, x: torch.Tensor,
+                        out_dtype=torch.bfloat16, y: Optional[torch.Tensor] = None,
+                        counts: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        stage_events=None):
+    """The layer forward over the slots of a replica plan, the shared expert
+    as one more routed group (dsmoe_moe_forward_serving).  Returns (y, counts).
+    stage_events: optional SERVING_STAGE_EVENTS raw hipEvent_t handles (ints)."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(bias, torch.float32, "bias")
+    _dev(slot_first, torch.int32, "slot_first")
+    _dev(slot_expert, torch.int32, "slot_expert")
+    T = x.shape[0]
+    S = slot_expert.numel()
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, desc.H), dtype=out_dtype, device=dev)
+    if counts is None:
+        counts = torch.empty((desc.E,), dtype=torch.int32, device=dev)
+    need = moe_serving_workspace_bytes(desc, T, S)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != SERVING_STAGE_EVENTS:
+            raise ValueError(f"stage_events needs {SERVING_STAGE_EVENTS} handles")
+        ev = (_vp * SERVING_STAGE_EVENTS)(*stage_events)
+    d = desc._c()
+    wc = slot_weights._c()
+    _check(lib.dsmoe_moe_forward_serving(ctypes.byref(d), ctypes.byref(wc), _p(slot_first), _p(slot_expert), S,
+                                         _p(bias), _p(x), T, _p(y), _dtype_code(y.dtype), _p(counts),
+                                         _p(workspace), workspace.numel(),
+                                         ctypes.cast(ev, ctypes.POINTER(_vp)) if ev is not None else None,
+                                         _stream()),
+           "dsmoe_moe_forward_serving")
+    return y, counts
 
 
 def update_bias(bias: torch.Tensor, counts: torch.Tensor, T: int, K: int, gamma: float = 0.001):

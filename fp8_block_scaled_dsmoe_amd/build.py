@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsmoe.so")
-SOURCES = ["abi.hip", "quant.hip", "granularity.hip", "route.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "quant.hip", "granularity.hip", "serving.hip", "route.hip", "gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

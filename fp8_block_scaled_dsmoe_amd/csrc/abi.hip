@@ -96,6 +96,28 @@ dsmoe_status check_desc(const dsmoe_moe_desc* d, int64_t T) {
   return DSMOE_OK;
 }
 
+// Workspace of dsmoe_moe_forward_serving: the forward's regions, then the
+// per-row gates of routed and shared rows and the slots' group offsets.
+struct ServingLayout {
+  Layout base;
+  size_t row_gate_all, phys, total;
+};
+
+ServingLayout serving_layout(const dsmoe_moe_desc& d, int64_t T, int32_t S) {
+  ServingLayout L{};
+  L.base = layout_for(d, T);
+  size_t off = L.base.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  L.row_gate_all = take((static_cast<size_t>(T) * d.K + (d.n_shared ? T : 0)) * 4);
+  L.phys = take((static_cast<size_t>(S) + 2) * 4);
+  L.total = off;
+  return L;
+}
+
 // Workspace layout of dsmoe_fp8_gemm_granularity (every region 256-byte
 // aligned): codes and the 1x128 / 128x128 scale layouts of both operands,
 // the per-row scales, the per-tensor scale and amax slots, the offsets {0, M}.
@@ -531,6 +553,187 @@ dsmoe_status dsmoe_fp8_gemm_granularity(const void* a, const void* w, int t, int
   p.rows_hint = M;
   DSMOE_TRY(dsmoe::launch_grouped_gemm(p, st));
   if (granularity == DSMOE_SCALE_CHANNEL) DSMOE_TRY(dsmoe::launch_scale_cols(c, M, N, row_w, st));
+#undef DSMOE_TRY
+  return DSMOE_OK;
+}
+
+dsmoe_status dsmoe_plan_replicas(const int32_t* counts, int32_t E, int32_t n_extra,
+                                 int32_t* slot_first, int32_t* slot_expert, void* stream) {
+  if (E < 1 || E > DSMOE_MAX_EXPERTS || n_extra < 0 || n_extra > DSMOE_MAX_EXPERTS)
+    return DSMOE_ERR_SHAPE;
+  if (!counts || !slot_first || !slot_expert) return DSMOE_ERR_NULL;
+  if (!aligned(counts, 4) || !aligned(slot_first, 4) || !aligned(slot_expert, 4)) return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  return launch_status(dsmoe::launch_plan_replicas(counts, E, n_extra, slot_first, slot_expert,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+dsmoe_status dsmoe_place_replicas(const uint8_t* w, const float* w_scale, int64_t N, int64_t K,
+                                  const int32_t* slot_expert, int32_t n_slots, uint8_t* w_slots,
+                                  float* s_slots, void* stream) {
+  if (N <= 0 || K <= 0 || N % 128 || K % 128 || n_slots < 0 || n_slots > 65535) return DSMOE_ERR_SHAPE;
+  if (N * K > (1LL << 40)) return DSMOE_ERR_SHAPE;
+  if (n_slots == 0) return DSMOE_OK;
+  if (!w || !w_scale || !slot_expert || !w_slots || !s_slots) return DSMOE_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(w_slots, 16) || !aligned(w_scale, 4) || !aligned(s_slots, 4) ||
+      !aligned(slot_expert, 4))
+    return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  return launch_status(dsmoe::launch_place_slots(w, w_scale, N, K, slot_expert, n_slots, w_slots, s_slots,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+dsmoe_status dsmoe_slot_offsets(const int32_t* offsets, int32_t E, const int32_t* slot_first,
+                                const int32_t* slot_expert, int32_t n_slots, int64_t extra_rows,
+                                int32_t* phys, void* stream) {
+  if (E < 1 || E > DSMOE_MAX_EXPERTS || n_slots < E || n_slots > E + DSMOE_MAX_EXPERTS)
+    return DSMOE_ERR_SHAPE;
+  if (extra_rows > kI32Max) return DSMOE_ERR_SHAPE;
+  if (!offsets || !slot_first || !slot_expert || !phys) return DSMOE_ERR_NULL;
+  if (!aligned(offsets, 4) || !aligned(slot_first, 4) || !aligned(slot_expert, 4) || !aligned(phys, 4))
+    return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  return launch_status(dsmoe::launch_slot_offsets(offsets, E, slot_first, slot_expert, n_slots,
+                                                  extra_rows < 0 ? -1 : extra_rows, phys,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+size_t dsmoe_moe_serving_workspace_bytes(const dsmoe_moe_desc* d, int64_t T, int32_t n_slots) {
+  if (check_desc(d, T) != DSMOE_OK) return 0;
+  if (n_slots < d->E || n_slots > d->E + DSMOE_MAX_EXPERTS) return 0;
+  return serving_layout(*d, T, n_slots).total;
+}
+
+dsmoe_status dsmoe_moe_forward_serving(const dsmoe_moe_desc* d, const dsmoe_moe_weights* w,
+                                       const int32_t* slot_first, const int32_t* slot_expert,
+                                       int32_t n_slots, const float* bias, const void* x, int64_t T,
+                                       void* y, int yt, int32_t* counts_out, void* workspace,
+                                       size_t ws_bytes, void* const* stage_events, void* stream) {
+  dsmoe_status s = check_desc(d, T);
+  if (s != DSMOE_OK) return s;
+  if (!valid_dtype(yt)) return DSMOE_ERR_DTYPE;
+  if (stage_events)
+    for (int i = 0; i < DSMOE_SERVING_STAGE_EVENTS; ++i)
+      if (!stage_events[i]) return DSMOE_ERR_NULL;
+  if (n_slots < d->E || n_slots > d->E + DSMOE_MAX_EXPERTS) return DSMOE_ERR_SHAPE;
+  if (T * (d->K + 1) + n_slots > kI32Max) return DSMOE_ERR_SHAPE;
+  if (!w || !bias || !counts_out || !slot_first || !slot_expert) return DSMOE_ERR_NULL;
+  if (!w->w13 || !w->s13 || !w->w2 || !w->s2 || !w->router_w) return DSMOE_ERR_NULL;
+  if (d->n_shared && (!w->w13_sh || !w->s13_sh || !w->w2_sh || !w->s2_sh)) return DSMOE_ERR_NULL;
+  if (T > 0 && (!x || !y)) return DSMOE_ERR_NULL;
+  const ServingLayout SL = serving_layout(*d, T, n_slots);
+  const Layout& L = SL.base;
+  if (T > 0 && !workspace) return DSMOE_ERR_WORKSPACE;
+  if (ws_bytes < SL.total) return DSMOE_ERR_WORKSPACE;
+  if ((x && !aligned(x, 16)) || (y && !aligned(y, 16)) || !aligned(w->w13, 16) ||
+      !aligned(w->w2, 16) || !aligned(w->router_w, 16) || !aligned(w->s13, 4) ||
+      !aligned(w->s2, 4) || !aligned(bias, 4) || !aligned(counts_out, 4) ||
+      !aligned(slot_first, 4) || !aligned(slot_expert, 4) || (workspace && !aligned(workspace, 256)))
+    return DSMOE_ERR_ALIGN;
+  if (d->n_shared && (!aligned(w->w13_sh, 16) || !aligned(w->w2_sh, 16) ||
+                      !aligned(w->s13_sh, 4) || !aligned(w->s2_sh, 4)))
+    return DSMOE_ERR_ALIGN;
+  s = check_device();
+  if (s != DSMOE_OK) return s;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t H = d->H, I = d->I;
+  const int32_t E = d->E, K = d->K;
+  const int64_t TK = T * K;
+  const int32_t sh = d->n_shared ? 1 : 0;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* qx = ws + L.qx;
+  float* sx = reinterpret_cast<float*>(ws + L.sx);
+  float* logits = reinterpret_cast<float*>(ws + L.logits);
+  int32_t* topk = reinterpret_cast<int32_t*>(ws + L.topk);
+  float* gates = reinterpret_cast<float*>(ws + L.gates);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* offsets_ext = reinterpret_cast<int32_t*>(ws + L.offsets_ext);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  uint8_t* qa = ws + L.qa;
+  float* sa = reinterpret_cast<float*>(ws + L.sa);
+  void* o = ws + L.o;
+  float* row_gate = reinterpret_cast<float*>(ws + SL.row_gate_all);
+  int32_t* phys = reinterpret_cast<int32_t*>(ws + SL.phys);
+
+#define DSMOE_TRY(expr)                                \
+  do {                                                 \
+    if ((expr) != hipSuccess) return DSMOE_ERR_LAUNCH; \
+  } while (0)
+  if (T == 0) {
+    DSMOE_TRY(dsmoe::launch_route_select(nullptr, bias, 0, E, d->G, d->Mg, K, nullptr, nullptr,
+                                         counts_out, st));
+    return DSMOE_OK;
+  }
+#define DSMOE_MARK(i) \
+  if (stage_events) DSMOE_TRY(hipEventRecord(static_cast<hipEvent_t>(stage_events[(i)]), st))
+  DSMOE_MARK(0);
+  // the steps of dsmoe_moe_forward up to the permute (perm extended by the
+  // shared expert's identity rows when n_shared = 1)
+  DSMOE_TRY(dsmoe::launch_quant_act(x, false, T, H, qx, sx, st));
+  DSMOE_TRY(dsmoe::launch_router_logits(static_cast<const uint16_t*>(x),
+                                        static_cast<const uint16_t*>(w->router_w), T, H, E, logits,
+                                        reinterpret_cast<float*>(ws + L.router_part), st));
+  DSMOE_TRY(dsmoe::launch_route_select(logits, bias, T, E, d->G, d->Mg, K, topk, gates, counts_out, st));
+  DSMOE_TRY(dsmoe::launch_permute(topk, gates, T, E, K, counts_out, offsets, perm, inv, row_gate,
+                                  sh ? offsets_ext : nullptr, st));
+  // the shared expert as a routed one: gate 1 on its rows
+  if (sh) DSMOE_TRY(dsmoe::launch_fill_f32(row_gate + TK, T, 1.0f, st));
+  // expert offsets -> slot offsets (and the shared group's end)
+  DSMOE_TRY(dsmoe::launch_slot_offsets(offsets, E, slot_first, slot_expert, n_slots, sh ? T : -1, phys, st));
+  DSMOE_MARK(1);
+
+  const int64_t rows = TK + (sh ? T : 0);
+  const int64_t hint = (TK + n_slots - 1) / n_slots;
+  dsmoe::GemmProblem g1{};
+  g1.a = qx;
+  g1.a_scale = sx;
+  g1.a_rows = perm;
+  g1.offsets = phys;
+  g1.G = n_slots + sh;
+  g1.M_total = rows;
+  g1.w = w->w13;
+  g1.w_scale = w->s13;
+  g1.w_last = sh ? w->w13_sh : nullptr;
+  g1.w_scale_last = sh ? w->s13_sh : nullptr;
+  g1.N = 2 * I;
+  g1.K = H;
+  g1.c = qa;
+  g1.c_scale = sa;
+  g1.epi = dsmoe::Epilogue::kSwiGLUQuant;
+  g1.row_limit = rows;
+  g1.rows_hint = hint;
+  DSMOE_TRY(dsmoe::launch_grouped_gemm(g1, st));
+  DSMOE_MARK(2);
+
+  dsmoe::GemmProblem g2{};
+  g2.a = qa;
+  g2.a_scale = sa;
+  g2.offsets = phys;
+  g2.G = n_slots + sh;
+  g2.M_total = rows;
+  g2.w = w->w2;
+  g2.w_scale = w->s2;
+  g2.w_last = sh ? w->w2_sh : nullptr;
+  g2.w_scale_last = sh ? w->s2_sh : nullptr;
+  g2.N = H;
+  g2.K = I;
+  g2.c = o;
+  g2.c_f32 = yt == DSMOE_F32;
+  g2.row_gate = row_gate;
+  g2.epi = dsmoe::Epilogue::kGateStore;
+  g2.row_limit = rows;
+  g2.rows_hint = hint;
+  DSMOE_TRY(dsmoe::launch_grouped_gemm(g2, st));
+  DSMOE_MARK(3);
+
+  DSMOE_TRY(dsmoe::launch_combine(o, inv, T, K, H, sh ? TK : -1, y, yt == DSMOE_F32, st));
+  DSMOE_MARK(4);
+#undef DSMOE_MARK
 #undef DSMOE_TRY
   return DSMOE_OK;
 }

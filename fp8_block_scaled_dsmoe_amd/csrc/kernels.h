@@ -31,6 +31,20 @@ hipError_t launch_broadcast_scale(float* dst, int64_t rows, int64_t tiles, const
 // c[m][n] *= col[n], float32 c [M][N], N % 4 == 0
 hipError_t launch_scale_cols(float* c, int64_t m, int64_t n, const float* col, hipStream_t s);
 
+// serving.hip
+// replica plan: slot_first [E+1], slot_expert [E + n_extra]; E <= 1024
+hipError_t launch_plan_replicas(const int32_t* counts, int32_t E, int32_t n_extra, int32_t* slot_first,
+                                int32_t* slot_expert, hipStream_t s);
+// group offsets of the S slots (+ the shared group when extra_rows >= 0): phys [S+2]
+hipError_t launch_slot_offsets(const int32_t* offsets, int32_t E, const int32_t* slot_first,
+                               const int32_t* slot_expert, int32_t S, int64_t extra_rows, int32_t* phys,
+                               hipStream_t s);
+// w_slots[s] = w[slot_expert[s]] ([N][K] codes and [N/128][K/128] scales)
+hipError_t launch_place_slots(const uint8_t* w, const float* w_scale, int64_t n, int64_t k,
+                              const int32_t* slot_expert, int32_t S, uint8_t* w_slots, float* s_slots,
+                              hipStream_t s);
+hipError_t launch_fill_f32(float* dst, int64_t n, float v, hipStream_t s);
+
 // route.hip
 // H is split over router_splits() blocks for small T; the splits' partial
 // sums go to `partial` (router_partial_bytes(), NULL when that is 0)

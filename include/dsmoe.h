@@ -277,6 +277,105 @@ dsmoe_status dsmoe_update_bias(float* bias, const int32_t* counts, int32_t E, in
                                int32_t K, float gamma, void* stream);
 
 /*
+ * Decode-serving variant.  Source: V3 notes §8, the deployment section (in
+ * decode the shared expert is a routed expert that every token takes, so a
+ * token uses 9 experts; some GPUs hold the shared expert and redundant
+ * copies of experts; the experts that run hot in live traffic are copied
+ * periodically, chosen from loads observed online, and the placement is
+ * adjusted); infra answer, inference paragraph (decode over 256 experts plus
+ * 64 copies of hot ones).  The pages fix neither how many copies an expert
+ * gets nor how a token picks a copy: the two rules below are this library's
+ * readings.
+ *
+ * A "slot" is one physical copy of a routed expert's weights.  The slots of
+ * one expert are consecutive: expert e owns slots slot_first[e] ..
+ * slot_first[e+1]-1 of S = slot_first[E], and slot_expert[s] names the
+ * expert of slot s.
+ */
+
+/*
+ * dsmoe_plan_replicas -- slots from observed loads.
+ *   counts       [E] int32 loads (e.g. counts_out of an earlier forward)
+ *   n_extra      slots beyond one per expert: S = E + n_extra
+ *   slot_first   [E+1] int32 (output)
+ *   slot_expert  [E + n_extra] int32 (output)
+ * Each extra slot goes, one at a time, to the expert with the largest load
+ * per slot counts[e] / n_e (compared exactly as integers; the lowest index
+ * wins ties), which minimises max_e counts[e] / n_e.  One wave on the device.
+ * Requires 1 <= E <= DSMOE_MAX_EXPERTS, 0 <= n_extra <= DSMOE_MAX_EXPERTS,
+ * counts >= 0.
+ */
+dsmoe_status dsmoe_plan_replicas(const int32_t* counts, int32_t E, int32_t n_extra,
+                                 int32_t* slot_first, int32_t* slot_expert, void* stream);
+
+/*
+ * dsmoe_place_replicas -- fill slot weights: w_slots[s] = w[slot_expert[s]].
+ *   w            [E][N][K] codes, w_scale [E][N/128][K/128] float32 (the
+ *                layouts of dsmoe_quant_w_128x128)
+ *   slot_expert  [n_slots] int32, each in [0, E) (read on the device as
+ *                given)
+ *   w_slots      [n_slots][N][K] codes, s_slots [n_slots][N/128][K/128]
+ *                (outputs; must not overlap the inputs)
+ * Call it for W13 and for W2 whenever the plan changes.  Requires N, K
+ * positive multiples of 128, 0 <= n_slots <= 65535.
+ */
+dsmoe_status dsmoe_place_replicas(const uint8_t* w, const float* w_scale, int64_t N, int64_t K,
+                                  const int32_t* slot_expert, int32_t n_slots, uint8_t* w_slots,
+                                  float* s_slots, void* stream);
+
+/*
+ * dsmoe_slot_offsets -- group offsets of the slots.
+ *   offsets      [E+1] int32 group offsets of the experts (e.g. from
+ *                dsmoe_route)
+ *   slot_first   [E+1], slot_expert [n_slots] int32: a plan
+ *   extra_rows   >= 0: rows of one more group after the routed rows (the
+ *                shared expert's), else -1
+ *   phys         [n_slots + 2] int32 (output): phys[s] for s < n_slots, then
+ *                phys[n_slots] = offsets[E] and, when extra_rows >= 0,
+ *                phys[n_slots + 1] = offsets[E] + extra_rows
+ * Slot slot_first[e] + j of expert e starts at row offsets[e] +
+ * floor(j * (offsets[e+1] - offsets[e]) / n_e): contiguous chunks that
+ * differ by at most one row.  Requires 1 <= E <= DSMOE_MAX_EXPERTS,
+ * E <= n_slots <= E + DSMOE_MAX_EXPERTS.
+ */
+dsmoe_status dsmoe_slot_offsets(const int32_t* offsets, int32_t E, const int32_t* slot_first,
+                                const int32_t* slot_expert, int32_t n_slots, int64_t extra_rows,
+                                int32_t* phys, void* stream);
+
+#define DSMOE_SERVING_STAGE_EVENTS 5
+
+/* Workspace of dsmoe_moe_forward_serving (0 for an invalid description). */
+size_t dsmoe_moe_serving_workspace_bytes(const dsmoe_moe_desc* d, int64_t T, int32_t n_slots);
+
+/*
+ * dsmoe_moe_forward_serving -- the layer forward over slots.
+ *   w            as in dsmoe_moe_forward, except that w13/s13/w2/s2 hold the
+ *                n_slots slots ([S][2I][H] codes, ...), filled by
+ *                dsmoe_place_replicas from the per-expert weights
+ *   slot_first   [E+1], slot_expert [n_slots] int32: the plan the slots were
+ *                placed with (slot_first[E] must equal n_slots)
+ *   stage_events NULL, or DSMOE_SERVING_STAGE_EVENTS hipEvent_t (created by
+ *                the caller) recorded on `stream` at the start, after the
+ *                permute, after the gate/up launch, after the down launch and
+ *                after the combine
+ *   everything else as in dsmoe_moe_forward (no debug copies)
+ * Routing, gates and counts_out (per expert) are those of dsmoe_moe_forward.
+ * The rows of expert e (its tokens, ascending) are cut into its n_e slots in
+ * contiguous chunks: slot slot_first[e] + j starts at row offsets[e] +
+ * floor(j * c_e / n_e).  With n_shared = 1 the shared expert runs as one more
+ * routed group, gate 1, in both GEMM launches (K + 1 experts per token).  y
+ * equals dsmoe_moe_forward's up to the float32 rounding of the GEMM tiles the
+ * launches pick (the same parity bar).
+ * Requires E <= n_slots <= E + DSMOE_MAX_EXPERTS and the limits of
+ * dsmoe_moe_forward.
+ */
+dsmoe_status dsmoe_moe_forward_serving(const dsmoe_moe_desc* d, const dsmoe_moe_weights* w,
+                                       const int32_t* slot_first, const int32_t* slot_expert,
+                                       int32_t n_slots, const float* bias, const void* x, int64_t T,
+                                       void* y, int yt, int32_t* counts_out, void* workspace,
+                                       size_t ws_bytes, void* const* stage_events, void* stream);
+
+/*
  * Coarser scaling granularities, for comparison with the recipe's 1x128 /
  * 128x128 tiles.  Source: infra answer, FP8 paragraph (per-tensor E4M3
  * scaling lets a single outlier stretch the scale of a whole tensor and so

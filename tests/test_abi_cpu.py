@@ -20,7 +20,7 @@ def _declared():
 def test_library_exports_every_declared_function():
     import fp8_block_scaled_dsmoe_amd as d
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(d.lib, n), f"{n} not exported"
     assert sorted(d.EXPORTED) == names
@@ -104,6 +104,40 @@ def test_granularity_validation_errors():
     assert G(a, None, 0, 64, 256, 512, 0, a, a, ws, None) == 1
     assert G(a, a, 0, 64, 256, 512, 0, a, _vp(ALIGNED + 16), ws, None) == 3    # workspace 256-aligned
     assert G(None, None, 0, 0, 256, 512, 1, None, None, 0, None) == 0          # M = 0: no-op
+
+
+def test_serving_validation_errors():
+    import fp8_block_scaled_dsmoe_amd as d
+    L = d.lib
+    a = _vp(ALIGNED)
+    assert L.dsmoe_plan_replicas(a, 0, 4, a, a, None) == 2
+    assert L.dsmoe_plan_replicas(a, 2000, 4, a, a, None) == 2
+    assert L.dsmoe_plan_replicas(a, 256, -1, a, a, None) == 2
+    assert L.dsmoe_plan_replicas(a, 256, 2000, a, a, None) == 2
+    assert L.dsmoe_plan_replicas(a, 256, 32, None, a, None) == 1
+    assert L.dsmoe_plan_replicas(a, 256, 32, a, _vp(MISALIGNED), None) == 3
+    assert L.dsmoe_place_replicas(a, a, 100, 128, a, 4, a, a, None) == 2
+    assert L.dsmoe_place_replicas(a, a, 128, 128, a, 70000, a, a, None) == 2
+    assert L.dsmoe_place_replicas(a, a, 128, 128, None, 4, a, a, None) == 1
+    assert L.dsmoe_place_replicas(a, a, 128, 128, a, 4, _vp(MISALIGNED), a, None) == 3
+    assert L.dsmoe_place_replicas(None, None, 128, 128, None, 0, None, None, None) == 0   # no slots: no-op
+    assert L.dsmoe_slot_offsets(a, 16, a, a, 15, -1, a, None) == 2                    # fewer slots than experts
+    assert L.dsmoe_slot_offsets(a, 16, a, a, 16 + 1025, -1, a, None) == 2
+    assert L.dsmoe_slot_offsets(a, 16, None, a, 20, -1, a, None) == 1
+    desc = d.MoEDesc(512, 256, 16, 4, 2, 2, 1)
+    assert d.moe_serving_workspace_bytes(desc, 256, 20) > d.moe_workspace_bytes(desc, 256)
+    assert d.moe_serving_workspace_bytes(desc, 256, 15) == 0
+    dc = desc._c()
+    wc = d._Weights(*([ALIGNED] * 9))
+    F = L.dsmoe_moe_forward_serving
+    ws = d.moe_serving_workspace_bytes(desc, 256, 20)
+    byref = ctypes.byref
+    assert F(byref(dc), byref(wc), a, a, 15, a, a, 256, a, 0, a, a, ws, None, None) == 2       # n_slots < E
+    assert F(byref(dc), byref(wc), None, a, 20, a, a, 256, a, 0, a, a, ws, None, None) == 1
+    assert F(byref(dc), byref(wc), a, a, 20, a, a, 256, a, 0, a, a, ws - 1, None, None) == 5
+    assert F(byref(dc), byref(wc), a, a, 20, a, a, 256, a, 9, a, a, ws, None, None) == 4
+    null_events = (ctypes.c_void_p * 5)()
+    assert F(byref(dc), byref(wc), a, a, 20, a, a, 256, a, 0, a, a, ws, null_events, None) == 1
 
 
 def test_route_and_bias_validation_errors():

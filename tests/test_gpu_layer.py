@@ -79,7 +79,16 @@ def _check_perm_valid(gpu, T, K, E):
         assert np.all(np.any(idx[seg] == e, axis=1))
 
 
-def _layer_case(cfg: LayerConfig, out_dtype, n_shared=1, seed=0):
+def _serving(d, desc, weights, counts, n_extra, bias, x, out_dtype):
+    """The serving forward with a replica plan from `counts` (n_extra extra
+    slots), the slot weights placed from `weights`."""
+    slot_first, slot_expert = d.plan_replicas(counts, n_extra)
+    slot_w = d.place_layer_replicas(weights, slot_expert)
+    y, c = d.moe_forward_serving(desc, slot_w, slot_first, slot_expert, bias, x, out_dtype=out_dtype)
+    return y, c, slot_first
+
+
+def _layer_case(cfg: LayerConfig, out_dtype, n_shared=1, seed=0, serving_extra=None):
     d = _dsmoe()
     inp = layer_inputs_host(cfg, seed)
     banner(f"layer {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} K={cfg.K} shared={n_shared} {out_dtype}")
@@ -123,6 +132,17 @@ def _layer_case(cfg: LayerConfig, out_dtype, n_shared=1, seed=0):
     yh = host(y)
     assert_normalised_close(yh[same], want["y"][same], want["y_d"][same], Y_TOL[out_dtype],
                             f"y {cfg.name} {out_dtype}", slack=want["y_slack"][same])
+    if serving_extra is not None:
+        # the decode-serving forward: slots planned from this step's loads, the
+        # shared expert as one more routed group; same routing, same bar
+        banner(f"layer {cfg.name} serving: {serving_extra} extra slots")
+        y2, c2, slot_first = _serving(d, desc, weights, counts, serving_extra, dev(inp["bias"]), x, out_dtype)
+        assert np.array_equal(host(c2), g["counts"])
+        n_rep = np.diff(host(slot_first))
+        print(f"[serving] slots per expert: max {n_rep.max()}, max rows per slot "
+              f"{(g['counts'] / n_rep).max():.1f} (was {g['counts'].max()})", flush=True)
+        assert_normalised_close(host(y2)[same], want["y"][same], want["y_d"][same], Y_TOL[out_dtype],
+                                f"y serving {cfg.name} {out_dtype}", slack=want["y_slack"][same])
     return y, counts
 
 
@@ -157,6 +177,30 @@ def test_layer_without_shared_expert():
     _layer_case(cfg, torch.float32, n_shared=0)
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("n_extra", [0, 1, 6, 40])
+def test_tiny_layer_serving(out_dtype, n_extra):
+    """The decode-serving forward on the tiny layer: no copies (the shared
+    expert as a routed group only), one, a few, and more copies than experts."""
+    _layer_case(LAYER_CONFIGS["tiny"], out_dtype, serving_extra=n_extra)
+
+
+@pytest.mark.parametrize("cfg", [
+    LayerConfig("ragged", T=77, H=256, E=8, G=2, Mg=1, K=3, I=128, router_std=0.05, bias_range=0.02),
+    LayerConfig("one_expert", T=130, H=384, E=1, G=1, Mg=1, K=1, I=256, router_std=0.05),
+    LayerConfig("few7", T=7, H=512, E=16, G=4, Mg=2, K=4, I=256, router_std=0.05),
+], ids=lambda c: c.name)
+def test_layer_shapes_serving(cfg):
+    """Serving with 3 extra slots: one expert cut into four, slots left empty
+    when an expert has fewer rows than slots (7 tokens)."""
+    _layer_case(cfg, torch.float32, serving_extra=3)
+
+
+def test_layer_serving_without_shared_expert():
+    cfg = LayerConfig("noshared", T=200, H=256, E=16, G=4, Mg=2, K=4, I=128, router_std=0.05)
+    _layer_case(cfg, torch.float32, n_shared=0, serving_extra=8)
+
+
 def test_layer_zero_tokens():
     d = _dsmoe()
     cfg = LAYER_CONFIGS["tiny"]
@@ -177,7 +221,7 @@ def test_layer_zero_tokens():
 # DeepSeek-V3 shapes at full size, checked on sampled tokens
 # ---------------------------------------------------------------------------
 
-def _v3_case(name: str, n_sample: int, out_dtype=torch.bfloat16):
+def _v3_case(name: str, n_sample: int, out_dtype=torch.bfloat16, serving_extra=None):
     d = _dsmoe()
     cfg = LAYER_CONFIGS[name]
     E, H, I = cfg.E, cfg.H, cfg.I
@@ -248,6 +292,13 @@ def _v3_case(name: str, n_sample: int, out_dtype=torch.bfloat16):
     yh = host(y)[toks]
     assert_normalised_close(yh[same], want["y"][same], want["y_d"][same], Y_TOL[out_dtype],
                             f"y {name} sampled", slack=want["y_slack"][same])
+    if serving_extra is not None:
+        banner(f"layer {name} serving: {serving_extra} extra slots")
+        y2, c2, _ = _serving(d, desc, weights, counts, serving_extra, dev(inp["bias"]),
+                             dev(inp["x"], torch.bfloat16), out_dtype)
+        assert np.array_equal(host(c2), g["counts"])
+        assert_normalised_close(host(y2)[toks][same], want["y"][same], want["y_d"][same], Y_TOL[out_dtype],
+                                f"y serving {name} sampled", slack=want["y_slack"][same])
     return g
 
 
@@ -257,6 +308,12 @@ def test_v3_prefill_full_size_sampled():
 
 def test_v3_decode_full_size_sampled():
     _v3_case("v3_decode", n_sample=4, out_dtype=torch.float32)
+
+
+def test_v3_decode_serving_full_size_sampled():
+    """The decode-serving forward at V3 decode size with 64 copies of hot
+    experts (the inference paragraph's 256 + 64) planned from this step's loads."""
+    _v3_case("v3_decode", n_sample=4, out_dtype=torch.float32, serving_extra=64)
 
 
 def test_v3_skew_full_size_sampled():
