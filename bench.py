@@ -73,8 +73,9 @@ def parse():
 
 
 COPY_BYTES = 1 << 30
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm1_swiglu_v3_prefill.json")
-GEMM_SOURCES = ["gemm.hip", "common.h", "kernels.h"]
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_gemm1_swiglu_{workload}.json")
+GEMM_SOURCES = ["gemm.hip", "common.h", "gemm.h"]
 
 
 def gemm_sources_sha256():
@@ -90,7 +91,7 @@ def measured_traffic(workload):
     """HBM bytes per launch of the gate/up GEMM from the committed counter runs,
     or None when they were taken on other kernel sources or another workload."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(traffic_file(workload)) as fh:
             t = json.load(fh)
     except OSError:
         return None

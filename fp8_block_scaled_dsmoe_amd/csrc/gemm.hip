@@ -31,7 +31,7 @@
 // tile order is remapped so that consecutive tiles land on the same XCD
 // (blocks are dispatched round-robin over the 8 XCDs) and share its L2.
 #include "common.h"
-#include "kernels.h"
+#include "gemm.h"
 
 namespace dsmoe {
 namespace {
