@@ -90,7 +90,7 @@ lib.dsmoe_fp8_gemm_granularity.argtypes = [_vp, _vp, _int, _i64, _i64, _i64, _in
 lib.dsmoe_plan_replicas.restype = _int
 lib.dsmoe_plan_replicas.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp]
 lib.dsmoe_place_replicas.restype = _int
-lib.dsmoe_place_replicas.argtypes = [_vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp]
+lib.dsmoe_place_replicas.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _vp]
 lib.dsmoe_slot_offsets.restype = _int
 lib.dsmoe_slot_offsets.argtypes = [_vp, _i32, _vp, _vp, _i32, _i64, _vp, _vp]
 lib.dsmoe_moe_serving_workspace_bytes.restype = _sz
@@ -443,11 +443,11 @@ def place_replicas(w: torch.Tensor, w_scale: torch.Tensor, slot_expert: torch.Te
     _dev(w, torch.uint8, "w")
     _dev(w_scale, torch.float32, "w_scale")
     _dev(slot_expert, torch.int32, "slot_expert")
-    _, n, k = w.shape
+    e, n, k = w.shape
     S = slot_expert.numel()
     w_slots = torch.empty((S, n, k), dtype=torch.uint8, device=w.device)
     s_slots = torch.empty((S, n // 128, k // 128), dtype=torch.float32, device=w.device)
-    _check(lib.dsmoe_place_replicas(_p(w), _p(w_scale), n, k, _p(slot_expert), S, _p(w_slots), _p(s_slots),
+    _check(lib.dsmoe_place_replicas(_p(w), _p(w_scale), e, n, k, _p(slot_expert), S, _p(w_slots), _p(s_slots),
                                     _stream()), "dsmoe_place_replicas")
     return w_slots, s_slots
 

@@ -569,10 +569,11 @@ dsmoe_status dsmoe_plan_replicas(const int32_t* counts, int32_t E, int32_t n_ext
                                                    static_cast<hipStream_t>(stream)));
 }
 
-dsmoe_status dsmoe_place_replicas(const uint8_t* w, const float* w_scale, int64_t N, int64_t K,
-                                  const int32_t* slot_expert, int32_t n_slots, uint8_t* w_slots,
-                                  float* s_slots, void* stream) {
-  if (N <= 0 || K <= 0 || N % 128 || K % 128 || n_slots < 0 || n_slots > 65535) return DSMOE_ERR_SHAPE;
+dsmoe_status dsmoe_place_replicas(const uint8_t* w, const float* w_scale, int32_t E, int64_t N,
+                                  int64_t K, const int32_t* slot_expert, int32_t n_slots,
+                                  uint8_t* w_slots, float* s_slots, void* stream) {
+  if (E < 1 || N <= 0 || K <= 0 || N % 128 || K % 128 || n_slots < 0 || n_slots > 65535)
+    return DSMOE_ERR_SHAPE;
   if (N * K > (1LL << 40)) return DSMOE_ERR_SHAPE;
   if (n_slots == 0) return DSMOE_OK;
   if (!w || !w_scale || !slot_expert || !w_slots || !s_slots) return DSMOE_ERR_NULL;
@@ -581,7 +582,7 @@ dsmoe_status dsmoe_place_replicas(const uint8_t* w, const float* w_scale, int64_
     return DSMOE_ERR_ALIGN;
   const dsmoe_status ds = check_device();
   if (ds != DSMOE_OK) return ds;
-  return launch_status(dsmoe::launch_place_slots(w, w_scale, N, K, slot_expert, n_slots, w_slots, s_slots,
+  return launch_status(dsmoe::launch_place_slots(w, w_scale, E, N, K, slot_expert, n_slots, w_slots, s_slots,
                                                  static_cast<hipStream_t>(stream)));
 }
 

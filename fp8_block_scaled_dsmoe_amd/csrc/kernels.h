@@ -42,7 +42,7 @@ hipError_t launch_slot_offsets(const int32_t* offsets, int32_t E, const int32_t*
                                const int32_t* slot_expert, int32_t S, int64_t extra_rows, int32_t* phys,
                                hipStream_t s);
 // w_slots[s] = w[slot_expert[s]] ([N][K] codes and [N/128][K/128] scales)
-hipError_t launch_place_slots(const uint8_t* w, const float* w_scale, int64_t n, int64_t k,
+hipError_t launch_place_slots(const uint8_t* w, const float* w_scale, int32_t E, int64_t n, int64_t k,
                               const int32_t* slot_expert, int32_t S, uint8_t* w_slots, float* s_slots,
                               hipStream_t s);
 hipError_t launch_fill_f32(float* dst, int64_t n, float v, hipStream_t s);

@@ -94,7 +94,10 @@ __global__ __launch_bounds__(kWave) void plan_replicas_kernel(const int32_t* __r
 
 // phys[s] for slots s < S from the experts' offsets; phys[S] = offsets[E];
 // phys[S + 1] = offsets[E] + extra_rows when extra_rows >= 0 (the shared
-// expert's rows after the routed ones).
+// expert's rows after the routed ones).  A slot whose plan entries are not
+// those of a plan (expert out of range, no slots, position outside the
+// expert's slots) gets offsets[E]: the results are then wrong, but every
+// offset stays inside the rows, so the GEMMs stay in bounds.
 __global__ __launch_bounds__(256) void slot_offsets_kernel(const int32_t* __restrict__ offsets, int32_t E,
                                                            const int32_t* __restrict__ slot_first,
                                                            const int32_t* __restrict__ slot_expert,
@@ -103,10 +106,15 @@ __global__ __launch_bounds__(256) void slot_offsets_kernel(const int32_t* __rest
   const int32_t s = static_cast<int32_t>(blockIdx.x) * 256 + threadIdx.x;
   if (s < S) {
     const int32_t e = slot_expert[s];
-    const int32_t j = s - slot_first[e];
-    const int32_t ne = slot_first[e + 1] - slot_first[e];
-    const int32_t cnt = offsets[e + 1] - offsets[e];
-    phys[s] = offsets[e] + static_cast<int32_t>(static_cast<int64_t>(j) * cnt / ne);
+    int32_t v = offsets[E];
+    if (e >= 0 && e < E) {
+      const int32_t j = s - slot_first[e];
+      const int32_t ne = slot_first[e + 1] - slot_first[e];
+      const int32_t cnt = offsets[e + 1] - offsets[e];
+      if (ne >= 1 && j >= 0 && j < ne && cnt >= 0)
+        v = offsets[e] + static_cast<int32_t>(static_cast<int64_t>(j) * cnt / ne);
+    }
+    phys[s] = v;
   } else if (s == S) {
     phys[S] = offsets[E];
     if (extra_rows >= 0) phys[S + 1] = offsets[E] + static_cast<int32_t>(extra_rows);
@@ -114,15 +122,17 @@ __global__ __launch_bounds__(256) void slot_offsets_kernel(const int32_t* __rest
 }
 
 // Slot s receives matrix slot_expert[s] and its block scales: a gather copy
-// in 16-byte words, blockIdx.y = slot.
+// in 16-byte words, blockIdx.y = slot.  A slot naming no expert in [0, E) is
+// left as it was.
 __global__ __launch_bounds__(256) void place_slots_kernel(const uint4* __restrict__ src, int64_t mat_words,
                                                           const float* __restrict__ src_scale,
                                                           int64_t mat_scales,
                                                           const int32_t* __restrict__ slot_expert,
-                                                          uint4* __restrict__ dst,
+                                                          int32_t E, uint4* __restrict__ dst,
                                                           float* __restrict__ dst_scale) {
   const int32_t s = blockIdx.y;
   const int64_t e = slot_expert[s];
+  if (e < 0 || e >= E) return;
   const uint4* from = src + e * mat_words;
   uint4* to = dst + static_cast<int64_t>(s) * mat_words;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
@@ -160,7 +170,7 @@ hipError_t launch_slot_offsets(const int32_t* offsets, int32_t E, const int32_t*
   return hipGetLastError();
 }
 
-hipError_t launch_place_slots(const uint8_t* w, const float* w_scale, int64_t n, int64_t k,
+hipError_t launch_place_slots(const uint8_t* w, const float* w_scale, int32_t E, int64_t n, int64_t k,
                               const int32_t* slot_expert, int32_t S, uint8_t* w_slots, float* s_slots,
                               hipStream_t s) {
   if (S == 0) return hipSuccess;
@@ -170,7 +180,7 @@ hipError_t launch_place_slots(const uint8_t* w, const float* w_scale, int64_t n,
   if (bx > 64) bx = 64;  // 64 blocks per slot: S * 64 blocks fill the chip for any S >= 32
   const dim3 grid(static_cast<unsigned>(bx), static_cast<unsigned>(S));
   place_slots_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const uint4*>(w), words, w_scale, scales,
-                                          slot_expert, reinterpret_cast<uint4*>(w_slots), s_slots);
+                                          slot_expert, E, reinterpret_cast<uint4*>(w_slots), s_slots);
   return hipGetLastError();
 }
 

@@ -312,16 +312,17 @@ dsmoe_status dsmoe_plan_replicas(const int32_t* counts, int32_t E, int32_t n_ext
  * dsmoe_place_replicas -- fill slot weights: w_slots[s] = w[slot_expert[s]].
  *   w            [E][N][K] codes, w_scale [E][N/128][K/128] float32 (the
  *                layouts of dsmoe_quant_w_128x128)
- *   slot_expert  [n_slots] int32, each in [0, E) (read on the device as
- *                given)
+ *   E            experts in w
+ *   slot_expert  [n_slots] int32, each in [0, E); a slot naming anything
+ *                else is left unwritten (checked on the device)
  *   w_slots      [n_slots][N][K] codes, s_slots [n_slots][N/128][K/128]
  *                (outputs; must not overlap the inputs)
  * Call it for W13 and for W2 whenever the plan changes.  Requires N, K
  * positive multiples of 128, 0 <= n_slots <= 65535.
  */
-dsmoe_status dsmoe_place_replicas(const uint8_t* w, const float* w_scale, int64_t N, int64_t K,
-                                  const int32_t* slot_expert, int32_t n_slots, uint8_t* w_slots,
-                                  float* s_slots, void* stream);
+dsmoe_status dsmoe_place_replicas(const uint8_t* w, const float* w_scale, int32_t E, int64_t N,
+                                  int64_t K, const int32_t* slot_expert, int32_t n_slots,
+                                  uint8_t* w_slots, float* s_slots, void* stream);
 
 /*
  * dsmoe_slot_offsets -- group offsets of the slots.
@@ -365,7 +366,9 @@ size_t dsmoe_moe_serving_workspace_bytes(const dsmoe_moe_desc* d, int64_t T, int
  * floor(j * c_e / n_e).  With n_shared = 1 the shared expert runs as one more
  * routed group, gate 1, in both GEMM launches (K + 1 experts per token).  y
  * equals dsmoe_moe_forward's up to the float32 rounding of the GEMM tiles the
- * launches pick (the same parity bar).
+ * launches pick (the same parity bar).  A plan that is not one (an expert
+ * index out of range, a slot outside its expert's range) gives unspecified
+ * results but no access outside the buffers.
  * Requires E <= n_slots <= E + DSMOE_MAX_EXPERTS and the limits of
  * dsmoe_moe_forward.
  */

@@ -116,11 +116,12 @@ def test_serving_validation_errors():
     assert L.dsmoe_plan_replicas(a, 256, 2000, a, a, None) == 2
     assert L.dsmoe_plan_replicas(a, 256, 32, None, a, None) == 1
     assert L.dsmoe_plan_replicas(a, 256, 32, a, _vp(MISALIGNED), None) == 3
-    assert L.dsmoe_place_replicas(a, a, 100, 128, a, 4, a, a, None) == 2
-    assert L.dsmoe_place_replicas(a, a, 128, 128, a, 70000, a, a, None) == 2
-    assert L.dsmoe_place_replicas(a, a, 128, 128, None, 4, a, a, None) == 1
-    assert L.dsmoe_place_replicas(a, a, 128, 128, a, 4, _vp(MISALIGNED), a, None) == 3
-    assert L.dsmoe_place_replicas(None, None, 128, 128, None, 0, None, None, None) == 0   # no slots: no-op
+    assert L.dsmoe_place_replicas(a, a, 8, 100, 128, a, 4, a, a, None) == 2
+    assert L.dsmoe_place_replicas(a, a, 8, 128, 128, a, 70000, a, a, None) == 2
+    assert L.dsmoe_place_replicas(a, a, 0, 128, 128, a, 4, a, a, None) == 2
+    assert L.dsmoe_place_replicas(a, a, 8, 128, 128, None, 4, a, a, None) == 1
+    assert L.dsmoe_place_replicas(a, a, 8, 128, 128, a, 4, _vp(MISALIGNED), a, None) == 3
+    assert L.dsmoe_place_replicas(None, None, 8, 128, 128, None, 0, None, None, None) == 0   # no slots: no-op
     assert L.dsmoe_slot_offsets(a, 16, a, a, 15, -1, a, None) == 2                    # fewer slots than experts
     assert L.dsmoe_slot_offsets(a, 16, a, a, 16 + 1025, -1, a, None) == 2
     assert L.dsmoe_slot_offsets(a, 16, None, a, 20, -1, a, None) == 1
