@@ -13,39 +13,12 @@
 // into the 1x128 / 128x128 layouts, and a per-output-channel weight scale,
 // which no 128x128 layout can hold, is applied to the finished output.
 #include "common.h"
+#include "encode.h"
 #include "kernels.h"
 
 namespace dsmoe {
 namespace {
 
-template <bool kF32>
-__device__ __forceinline__ void load8(const void* base, int64_t idx, float (&v)[8]) {
-  if constexpr (kF32) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
-    const float4 a = p[0];
-    const float4 b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  }
-}
-
-__device__ __forceinline__ uint2 encode8(const float (&v)[8], float s) {
-  const uint32_t c01 = e4m3_encode2(v[0] / s, v[1] / s), c23 = e4m3_encode2(v[2] / s, v[3] / s);
-  const uint32_t c45 = e4m3_encode2(v[4] / s, v[5] / s), c67 = e4m3_encode2(v[6] / s, v[7] / s);
-  return make_uint2(c01 | (c23 << 16), c45 | (c67 << 16));
-}
-
-__device__ __forceinline__ float scale_from_amax(float amax) {
-  return amax == 0.0f ? 1.0f : amax / 448.0f;
-}
 
 __device__ __forceinline__ float amax8(const float (&v)[8], float m) {
 #pragma unroll

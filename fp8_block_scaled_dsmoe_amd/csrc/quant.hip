@@ -8,42 +8,12 @@
 // Both kernels are HBM-streaming: every input byte is read once (16-byte
 // loads) and every code written once.
 #include "common.h"
+#include "encode.h"
 #include "kernels.h"
 
 namespace dsmoe {
 namespace {
 
-template <bool kF32>
-__device__ __forceinline__ void load8(const void* base, int64_t idx, float (&v)[8]) {
-  if constexpr (kF32) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
-    const float4 a = p[0];
-    const float4 b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  }
-}
-
-// Codes of v / s (IEEE division, then round to nearest even).  |v / s| <=
-// 448 (1 + 2^-23) for the scales used here (s = amax / 448), well inside the
-// range where the packed hardware conversion gives e4m3_encode's code.
-__device__ __forceinline__ uint2 encode8(const float (&v)[8], float s) {
-  const uint32_t c01 = e4m3_encode2(v[0] / s, v[1] / s), c23 = e4m3_encode2(v[2] / s, v[3] / s);
-  const uint32_t c45 = e4m3_encode2(v[4] / s, v[5] / s), c67 = e4m3_encode2(v[6] / s, v[7] / s);
-  return make_uint2(c01 | (c23 << 16), c45 | (c67 << 16));
-}
-
-__device__ __forceinline__ float scale_from_amax(float amax) {
-  return amax == 0.0f ? 1.0f : amax / 448.0f;
-}
 
 // Maximum of non-negative values over each aligned group of 8 lanes, left
 // in every lane of the group: swap neighbours, swap pairs (quad
@@ -60,9 +30,10 @@ __device__ __forceinline__ float row8_max_nonneg(float v) {
 // 8 lanes per 1x128 tile, 16 elements per lane (one 16-byte store of codes
 // per lane), 32 tiles per block.  Rows are contiguous, so tile t of the
 // [rows][cols/128] grid starts at element 128 t and its scale is scale[t].
-// Measured on MI355X (4096 x 7168 bf16): 18.3 us, against 20.2 us with 16
-// lanes of 8 elements and 8-byte stores, and 13.5 us for a kernel that moves
-// the same bytes with no arithmetic; the rest is the IEEE divisions.
+// Measured on MI355X (4096 x 7168 bf16, with an IEEE division per element):
+// 18.3 us, against 20.2 us with 16 lanes of 8 elements and 8-byte stores, and
+// 13.5 us for a kernel that moves the same bytes with no arithmetic (and no
+// amax reduction between its loads and stores).
 template <bool kF32>
 __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__ x, int64_t n_tiles,
                                                         uint8_t* __restrict__ q,

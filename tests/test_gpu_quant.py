@@ -111,3 +111,60 @@ def test_weights_v3_expert_shape():
     qo, so = oq.quant_w_128x128(w13)
     assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
     assert np.array_equal(host(q), qo)
+
+
+def _near_rounding_points(amax: float, seed: int) -> np.ndarray:
+    """float32 tiles [n][128] whose element 0 is `amax` (so every tile has
+    s = fl32(amax / 448), not a power of two) and whose other elements put
+    v / s within 3 float32 ulps of an E4M3 rounding point (the midpoint of two
+    neighbouring codes), both signs, normal and subnormal codes alike."""
+    from oracle import e4m3
+    vals = e4m3.decode(np.arange(0, 127, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    s = np.float32(np.float32(amax) / np.float32(448.0))
+    out = []
+    for m in mids:
+        v0 = np.float32(np.float64(m) * np.float64(s))
+        for k in range(-3, 4):
+            v = v0
+            for _ in range(abs(k)):
+                v = np.nextafter(v, np.float32(np.inf if k > 0 else -np.inf), dtype=np.float32)
+            out += [v, -v]
+    out = np.array(out, np.float32)
+    out = out[np.random.default_rng(seed).permutation(len(out))]
+    n = -(-len(out) // 127)
+    body = np.zeros(n * 127, np.float32)
+    body[:len(out)] = out
+    x = np.empty((n, 128), np.float32)
+    x[:, 0] = np.float32(amax)
+    x[:, 1:] = body.reshape(n, 127)
+    return x
+
+
+@pytest.mark.parametrize("amax", [448 * 1.37, 448 * 0.731, 448 * 3.3e-3, 448 * 7.77e4, 1.0e-3])
+def test_codes_near_rounding_points_with_a_general_scale(amax):
+    """Every quotient v / s lies within a few float32 ulps of an E4M3 rounding
+    point, with a scale that is not a power of two: the codes must be those of
+    the IEEE quotient (a reciprocal multiply would get some of them wrong)."""
+    d = _dsmoe()
+    from oracle import granularity as og
+    x = _near_rounding_points(amax, seed=int(amax * 1000) % 9973)
+    banner(f"near rounding points amax={amax} tiles={x.shape[0]}")
+    _check_act(x.reshape(-1, 256) if x.shape[0] % 2 == 0 else x, False, f"near-midpoint act amax={amax}")
+    # the same values as 128x128 weight blocks
+    nb = x.shape[0] // 128 * 128
+    if nb:
+        w = x[:nb].reshape(nb // 128, 128, 128).transpose(1, 0, 2).reshape(128, -1)
+        wt = dev(np.ascontiguousarray(w), torch.float32)
+        q, s = d.quant_w_128x128(wt)
+        qo, so = oq.quant_w_128x128(w)
+        assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+        assert np.array_equal(host(q), qo)
+    # per row (each row holds amax) and per tensor
+    q, s = d.quant_rows(dev(x, torch.float32))
+    qo, so = og.quant_rows(x)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), qo)
+    q, s, _ = d.quant_tensor(dev(x, torch.float32))
+    qo, so = og.quant_tensor(x)
+    assert host(s)[0] == so and np.array_equal(host(q), qo)
