@@ -65,7 +65,7 @@ def parse():
                     help="v3_decode_serving: copies of hot experts beyond one slot per expert")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=10)
+    ap.add_argument("--cpu-tokens", type=int, default=14)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times): the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
