@@ -538,7 +538,7 @@ def run_serving(args, torch):
                                f"top-{K} within {cfg.Mg} of {cfg.G} groups, I={I}, y {args.out_dtype}",
                    "T": T, "H": H, "E": E, "G": cfg.G, "Mg": cfg.Mg, "K": K, "I": I, "slots": S},
         "roofline": {"bound": "hbm", "achieved": round(g1_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(g1_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(g1_gbps / PEAK_HBM_GBPS, 4), "traffic": measured_traffic("v3_decode_serving"),
                      "kernel": "gate/up grouped FP8 GEMM + SwiGLU + 1x128 requant over the slots (one launch)",
                      "algorithmic_bytes": int(g1_bytes), "avg_ms": round(g1_ms, 4)},
         "layer_hbm_gbps": round(layer_gbps, 1),
