@@ -190,3 +190,42 @@ def test_moe_forward_validation_errors():
     assert call({"d": ctypes.byref(bad)}) == 2
     w_null = d._Weights(*([ALIGNED] * 4 + [None] + [ALIGNED] * 4))
     assert call({"w": ctypes.byref(w_null)}) == 1
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include "dsmoe.h"
+int main(void) {
+  dsmoe_moe_desc d = {7168, 2048, 256, 8, 4, 8, 1};
+  if (dsmoe_abi_version() != 1) return 1;
+  if (dsmoe_moe_workspace_bytes(&d, 4096) == 0) return 2;
+  if (dsmoe_moe_serving_workspace_bytes(&d, 64, 320) == 0) return 3;
+  if (dsmoe_gemm_granularity_workspace_bytes(4096, 4096, 7168) == 0) return 4;
+  if (dsmoe_quant_rows(NULL, DSMOE_BF16, 4, 100, NULL, NULL, NULL) != DSMOE_ERR_SHAPE) return 5;
+  if (dsmoe_plan_replicas(NULL, 0, 0, NULL, NULL, NULL) != DSMOE_ERR_SHAPE) return 6;
+  puts(dsmoe_status_str(DSMOE_ERR_WORKSPACE));
+  return 0;
+}
+"""
+
+
+def test_header_is_c99_and_links_from_c(tmp_path):
+    """include/dsmoe.h is a C header: a C99 program compiles against it, links
+    to libdsmoe.so and makes host-only calls (no device work)."""
+    import shutil
+    import subprocess
+    import fp8_block_scaled_dsmoe_amd as d
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(d.LIB_PATH)
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I",
+                        os.path.join(ROOT, "include"), str(src), "-L", libdir, "-ldsmoe",
+                        f"-Wl,-rpath,{libdir}", "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, (out.returncode, out.stderr)
+    assert out.stdout.strip() == "DSMOE_ERR_WORKSPACE"
