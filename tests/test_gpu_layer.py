@@ -310,6 +310,13 @@ def test_v3_decode_full_size_sampled():
     _v3_case("v3_decode", n_sample=4, out_dtype=torch.float32)
 
 
+def test_v3_prefill_serving_full_size_sampled():
+    """The serving forward at V3 prefill size (T = 4096, groups of ~128 rows
+    split over 32 extra slots, the shared expert's 4096 rows as one group of
+    the routed launches)."""
+    _v3_case("v3_prefill", n_sample=4, serving_extra=32)
+
+
 def test_v3_decode_serving_full_size_sampled():
     """The decode-serving forward at V3 decode size with 64 copies of hot
     experts (the inference paragraph's 256 + 64) planned from this step's loads."""
