@@ -15,6 +15,15 @@ decode batch (T=64) through dsmoe_moe_forward_serving: the shared expert as a
 placed once before timing.  A step is the serving forward plus the bias
 update; the plain decode step is timed in the same process for comparison.
 
+The data-gradient workload (--workload v3_prefill_dgrad) times the FP8
+dgrad GEMMs of the routed experts at V3 prefill size on the batch's own
+routing: the block transposes of W2 and W13 (dsmoe_transpose_w_128x128), then
+dA = dy . W2 over the permuted rows (dy quantised 1x128 along H, rows gathered
+by token) and dx_rows = dh . W13 (dh quantised 1x128 along 2I), both with
+dsmoe_fp8_grouped_gemm on the transposed weights.  dy and dh are seeded
+N(0, 1) bf16 stand-ins: the SwiGLU backward that would produce dh is not part
+of it.
+
 The granularity workload (--workload c2_granularity) runs the same GEMM
 end to end from the bf16 operands at three scaling granularities (one scale
 per tensor, per token x per output channel, and the recipe's 1x128 / 128x128
@@ -60,7 +69,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="v3_prefill",
                     choices=["v3_prefill", "v3_decode", "v3_skew", "tiny", "c2_dense", "c2_granularity",
-                             "v3_decode_serving"])
+                             "v3_decode_serving", "v3_prefill_dgrad"])
     ap.add_argument("--extra-slots", type=int, default=64,
                     help="v3_decode_serving: copies of hot experts beyond one slot per expert")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
@@ -566,6 +575,88 @@ def run_serving(args, torch):
     print(json.dumps(result), flush=True)
 
 
+def run_dgrad(args, torch):
+    import fp8_block_scaled_dsmoe_amd as d
+    import dsmoe_inputs as dsi
+    cfg = dsi.LAYER_CONFIGS["v3_prefill"]
+    T, H, I, E, K = cfg.T, cfg.H, cfg.I, cfg.E, cfg.K
+    TK = T * K
+    log(f"workload v3_prefill_dgrad: T={T} H={H} E={E} K={K} I={I}, routed experts")
+    x, bias, weights, _ = build_layer(cfg, d, torch, dsi)
+    desc = d.MoEDesc(H, I, E, cfg.G, cfg.Mg, K, 1)
+    _, counts, dbg = d.moe_forward(desc, weights, bias, x, debug=True)
+    perm, offsets = dbg["perm"], dbg["offsets"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    dy = torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16)
+    dh = torch.randn((TK, 2 * I), device="cuda", generator=g).to(torch.bfloat16)
+    qdy, sdy = d.quant_act_1x128(dy)
+    qdh, sdh = d.quant_act_1x128(dh)
+    w2t, s2t = d.transpose_w_128x128(weights.w2, weights.s2)
+    w13t, s13t = d.transpose_w_128x128(weights.w13, weights.s13)
+    da = torch.empty((TK, I), dtype=torch.float32, device="cuda")
+    dxr = torch.empty((TK, H), dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    t_w2 = timed(lambda: d.transpose_w_128x128(weights.w2, weights.s2))
+    t_w13 = timed(lambda: d.transpose_w_128x128(weights.w13, weights.s13))
+    t_down = timed(lambda: d.fp8_grouped_gemm(qdy, sdy, offsets, w2t, s2t, a_rows=perm, m_total=TK, c=da))
+    t_up = timed(lambda: d.fp8_grouped_gemm(qdh, sdh, offsets, w13t, s13t, c=dxr))
+    touched = int((counts > 0).sum().item())
+    fl_down = 2.0 * TK * H * I
+    fl_up = 2.0 * TK * 2 * I * H
+    b_down = touched * H * I + TK * I * 4 + T * H       # W2^T streamed, f32 out, dy codes
+    b_up = touched * 2 * I * H + TK * H * 2 + TK * 2 * I  # W13^T streamed, bf16 out, dh codes
+    gb = lambda b, ms: b / (ms * 1e-3) / 1e9
+    tf = lambda f, ms: f / (ms * 1e-3) / 1e12
+    tr_bytes_w2, tr_bytes_w13 = 2 * E * H * I, 2 * E * 2 * I * H
+    log(f"transpose W2 {t_w2:.3f} ms ({gb(tr_bytes_w2, t_w2):.0f} GB/s), W13 {t_w13:.3f} ms "
+        f"({gb(tr_bytes_w13, t_w13):.0f} GB/s)")
+    log(f"dgrad down (dy.W2) {t_down:.3f} ms: {tf(fl_down, t_down):.0f} TFLOP/s, {gb(b_down, t_down):.0f} GB/s; "
+        f"dgrad up (dh.W13) {t_up:.3f} ms: {tf(fl_up, t_up):.0f} TFLOP/s, {gb(b_up, t_up):.0f} GB/s")
+    ms = t_down + t_up
+    result = {
+        "metric": METRIC,
+        "value": round(tf(fl_down + fl_up, ms), 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"v3_prefill_dgrad: FP8 data-gradient grouped GEMMs of the routed experts, "
+                               f"dy.W2 and dh.W13 on block-transposed weights, T={T}, H={H}, E={E}, "
+                               f"top-{K}, I={I}", "T": T, "H": H, "E": E, "K": K, "I": I},
+        "roofline": {"bound": "hbm", "achieved": round(gb(b_up, t_up), 2), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(gb(b_up, t_up) / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "dgrad of the gate/up projection, dh . W13 (grouped FP8 GEMM)",
+                     "algorithmic_bytes": int(b_up), "algorithmic_flops": fl_up, "avg_ms": round(t_up, 4)},
+        "dgrad_down": {"ms": round(t_down, 4), "tflops": round(tf(fl_down, t_down), 2),
+                       "gbps": round(gb(b_down, t_down), 1), "algorithmic_bytes": int(b_down)},
+        "transpose_ms": {"w2": round(t_w2, 4), "w13": round(t_w13, 4),
+                         "gbps": round(gb(tr_bytes_w2 + tr_bytes_w13, t_w2 + t_w13), 1)},
+        "experts_touched": touched,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -584,6 +675,9 @@ def main():
         return
     if args.workload == "v3_decode_serving":
         run_serving(args, torch)
+        return
+    if args.workload == "v3_prefill_dgrad":
+        run_dgrad(args, torch)
         return
     import fp8_block_scaled_dsmoe_amd as d
     import dsmoe_inputs as dsi

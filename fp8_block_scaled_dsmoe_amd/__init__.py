@@ -24,7 +24,7 @@ __all__ = [
     "moe_workspace_bytes", "moe_forward", "update_bias", "quantize_layer_weights",
     "quant_rows", "quant_tensor", "gemm_granularity_workspace_bytes", "fp8_gemm_granularity",
     "GRANULARITIES", "plan_replicas", "place_replicas", "place_layer_replicas", "slot_offsets",
-    "moe_serving_workspace_bytes", "moe_forward_serving", "BF16", "F32",
+    "moe_serving_workspace_bytes", "moe_forward_serving", "transpose_w_128x128", "BF16", "F32",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsmoe.so")
@@ -91,6 +91,8 @@ lib.dsmoe_plan_replicas.restype = _int
 lib.dsmoe_plan_replicas.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp]
 lib.dsmoe_place_replicas.restype = _int
 lib.dsmoe_place_replicas.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _vp]
+lib.dsmoe_transpose_w_128x128.restype = _int
+lib.dsmoe_transpose_w_128x128.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]
 lib.dsmoe_slot_offsets.restype = _int
 lib.dsmoe_slot_offsets.argtypes = [_vp, _i32, _vp, _vp, _i32, _i64, _vp, _vp]
 lib.dsmoe_moe_serving_workspace_bytes.restype = _sz
@@ -106,7 +108,7 @@ EXPORTED = ("dsmoe_status_str", "dsmoe_abi_version", "dsmoe_quant_act_1x128", "d
             "dsmoe_update_bias", "dsmoe_quant_rows", "dsmoe_quant_tensor",
             "dsmoe_gemm_granularity_workspace_bytes", "dsmoe_fp8_gemm_granularity",
             "dsmoe_plan_replicas", "dsmoe_place_replicas", "dsmoe_slot_offsets", "dsmoe_moe_serving_workspace_bytes",
-            "dsmoe_moe_forward_serving")
+            "dsmoe_moe_forward_serving", "dsmoe_transpose_w_128x128")
 
 # dsmoe_granularity codes
 GRANULARITIES = {"tensor": 0, "channel": 1, "block": 2}
@@ -192,6 +194,22 @@ def quant_w_128x128(w: torch.Tensor, q: Optional[torch.Tensor] = None,
     if squeeze:
         return q[0], scale[0]
     return q, scale
+
+
+def transpose_w_128x128(q: torch.Tensor, s: torch.Tensor):
+    """Codes [n_mats][N][K] (or [N][K]) and their 128x128 scales -> those of
+    W^T: codes [..][K][N], scales [..][K/128][N/128] (dsmoe_transpose_w_128x128)."""
+    squeeze = q.dim() == 2
+    q3 = q.unsqueeze(0) if squeeze else q
+    s3 = s.unsqueeze(0) if squeeze else s
+    _dev(q3, torch.uint8, "q")
+    _dev(s3, torch.float32, "s")
+    nm, n, k = q3.shape
+    qt = torch.empty((nm, k, n), dtype=torch.uint8, device=q.device)
+    st = torch.empty((nm, k // 128, n // 128), dtype=torch.float32, device=q.device)
+    _check(lib.dsmoe_transpose_w_128x128(_p(q3), _p(s3), nm, n, k, _p(qt), _p(st), _stream()),
+           "dsmoe_transpose_w_128x128")
+    return (qt[0], st[0]) if squeeze else (qt, st)
 
 
 def route(logits: torch.Tensor, bias: torch.Tensor, n_groups: int, groups_kept: int, top_k: int):

@@ -205,6 +205,18 @@ dsmoe_status dsmoe_quant_w_128x128(const void* w, int wt, int64_t n_mats, int64_
                                              static_cast<hipStream_t>(stream)));
 }
 
+dsmoe_status dsmoe_transpose_w_128x128(const uint8_t* q, const float* s, int64_t n_mats, int64_t N,
+                                       int64_t K, uint8_t* qt, float* st, void* stream) {
+  if (n_mats < 0 || N <= 0 || K <= 0 || N % 128 || K % 128) return DSMOE_ERR_SHAPE;
+  if (n_mats * (N / 128) * (K / 128) >= kI32Max || N * K > (1LL << 40)) return DSMOE_ERR_SHAPE;
+  if (n_mats == 0) return DSMOE_OK;
+  if (!q || !s || !qt || !st) return DSMOE_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(qt, 16) || !aligned(s, 4) || !aligned(st, 4)) return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  return launch_status(dsmoe::launch_transpose_w(q, s, n_mats, N, K, qt, st, static_cast<hipStream_t>(stream)));
+}
+
 dsmoe_status dsmoe_route(const float* logits, const float* bias, int64_t T, int32_t E, int32_t G,
                          int32_t Mg, int32_t K, int32_t* topk_idx, float* gates, int32_t* counts,
                          int32_t* offsets, int32_t* perm, int32_t* inv, void* stream) {

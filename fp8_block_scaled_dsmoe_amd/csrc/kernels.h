@@ -15,6 +15,9 @@ hipError_t launch_quant_act(const void* x, bool x_f32, int64_t rows, int64_t col
                             float* scale, hipStream_t s);
 hipError_t launch_quant_w(const void* w, bool w_f32, int64_t n_mats, int64_t n, int64_t k,
                           uint8_t* q, float* scale, hipStream_t s);
+// codes [n_mats][n][k] + 128x128 scales -> codes [n_mats][k][n] + scales of W^T
+hipError_t launch_transpose_w(const uint8_t* q, const float* s, int64_t n_mats, int64_t n, int64_t k,
+                              uint8_t* qt, float* st, hipStream_t stream);
 
 // granularity.hip
 int64_t quant_rows_max_cols();

@@ -92,6 +92,66 @@ __global__ __launch_bounds__(256) void quant_w_kernel(const void* __restrict__ w
   if (threadIdx.x == 0) scale[mat * nb * kb + bi * kb + bj] = s;
 }
 
+// W^T from W's 128x128-block codes and scales: a block's amax does not change
+// under transposition, so the codes move and nothing is requantised (the
+// weight operand of a data-gradient GEMM).  One 256-thread block per 128x128
+// code block: coalesced 16-byte row loads into an LDS tile, 4x4-byte
+// sub-blocks transposed in registers with byte permutes, a second LDS tile,
+// coalesced 16-byte row stores.  Tiles are 33 dwords a row so that the
+// column-wise accesses of a wave spread over the banks.
+__global__ __launch_bounds__(256) void transpose_blocks_kernel(const uint8_t* __restrict__ q,
+                                                               const float* __restrict__ s, int64_t n,
+                                                               int64_t k, uint8_t* __restrict__ qt,
+                                                               float* __restrict__ st) {
+  __shared__ uint32_t tin[kTile * 33];
+  __shared__ uint32_t tout[kTile * 33];
+  const int64_t nb = n / kTile, kb = k / kTile;
+  const int64_t blk = blockIdx.x;
+  const int64_t mat = blk / (nb * kb);
+  const int64_t rem = blk - mat * nb * kb;
+  const int64_t bi = rem / kb, bj = rem - bi * kb;  // block row of W [n][k], block column
+  const uint8_t* src = q + mat * n * k + (bi * kTile) * k + bj * kTile;
+  uint8_t* dst = qt + mat * n * k + (bj * kTile) * n + bi * kTile;  // W^T is [k][n]
+  const int t = threadIdx.x;
+  const int r = t >> 1, c0 = (t & 1) * 16;  // row, first dword of its 64-byte half
+  {
+    const uint4* p = reinterpret_cast<const uint4*>(src + static_cast<int64_t>(r) * k + c0 * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = p[i];
+      uint32_t* d = &tin[r * 33 + c0 + 4 * i];
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+  }
+  __syncthreads();
+  const int sc = t & 31;  // dword column of the input tile = 4 output rows
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sr = (t >> 5) + 8 * i;  // 4 input rows = one output dword column
+    const uint32_t d0 = tin[(4 * sr + 0) * 33 + sc], d1 = tin[(4 * sr + 1) * 33 + sc];
+    const uint32_t d2 = tin[(4 * sr + 2) * 33 + sc], d3 = tin[(4 * sr + 3) * 33 + sc];
+    // byte j of output dword m = byte m of input dword j
+    const uint32_t lo01 = __builtin_amdgcn_perm(d1, d0, 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(d1, d0, 0x07030602u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+    tout[(4 * sc + 0) * 33 + sr] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    tout[(4 * sc + 1) * 33 + sr] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    tout[(4 * sc + 2) * 33 + sr] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    tout[(4 * sc + 3) * 33 + sr] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+  }
+  __syncthreads();
+  {
+    uint4* p = reinterpret_cast<uint4*>(dst + static_cast<int64_t>(r) * n + c0 * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t* d = &tout[r * 33 + c0 + 4 * i];
+      p[i] = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+  }
+  if (t == 0) st[mat * kb * nb + bj * nb + bi] = s[mat * nb * kb + bi * kb + bj];
+}
+
 }  // namespace
 
 hipError_t launch_quant_act(const void* x, bool x_f32, int64_t rows, int64_t cols, uint8_t* q,
@@ -115,6 +175,18 @@ hipError_t launch_quant_w(const void* w, bool w_f32, int64_t n_mats, int64_t n, 
     quant_w_kernel<true><<<grid, 256, 0, s>>>(w, n, k, q, scale);
   else
     quant_w_kernel<false><<<grid, 256, 0, s>>>(w, n, k, q, scale);
+  return hipGetLastError();
+}
+
+}  // namespace dsmoe
+
+namespace dsmoe {
+
+hipError_t launch_transpose_w(const uint8_t* q, const float* s, int64_t n_mats, int64_t n, int64_t k,
+                              uint8_t* qt, float* st, hipStream_t stream) {
+  const int64_t blocks = n_mats * (n / kTile) * (k / kTile);
+  if (blocks == 0) return hipSuccess;
+  transpose_blocks_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(q, s, n, k, qt, st);
   return hipGetLastError();
 }
 

@@ -104,6 +104,24 @@ dsmoe_status dsmoe_quant_w_128x128(const void* w, int wt, int64_t n_mats, int64_
                                    uint8_t* q, float* scale, void* stream);
 
 /*
+ * dsmoe_transpose_w_128x128 -- the weight operand of a data-gradient GEMM.
+ * Source: V3 notes §6 (the activation-gradient GEMM runs in FP8 like the
+ * forward) and §6.1 (128x128 weight blocks).  A block's amax does not change
+ * under transposition, so W^T's codes and block scales are W's, moved:
+ *
+ *   q      [n_mats][N][K] codes, s [n_mats][N/128][K/128] float32 (as from
+ *          dsmoe_quant_w_128x128)
+ *   qt     [n_mats][K][N] codes (output), st [n_mats][K/128][N/128] (output);
+ *          must not overlap the inputs
+ *
+ * With qt/st as the weight, dsmoe_fp8_grouped_gemm computes dA = dC . W (the
+ * gradient of c = A W^T with respect to A) from the 1x128 codes of dC.
+ * Requires N, K positive multiples of 128, n_mats >= 0.
+ */
+dsmoe_status dsmoe_transpose_w_128x128(const uint8_t* q, const float* s, int64_t n_mats, int64_t N,
+                                       int64_t K, uint8_t* qt, float* st, void* stream);
+
+/*
  * dsmoe_route -- auxiliary-loss-free, group-limited top-K routing and the
  * token permute.
  * Source: V3 notes §4 (top-K chosen on s + b, gate weights from the raw

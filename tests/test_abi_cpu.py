@@ -20,7 +20,7 @@ def _declared():
 def test_library_exports_every_declared_function():
     import fp8_block_scaled_dsmoe_amd as d
     names = _declared()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(d.lib, n), f"{n} not exported"
     assert sorted(d.EXPORTED) == names
@@ -70,6 +70,12 @@ def test_quant_validation_errors():
     assert L.dsmoe_quant_w_128x128(_vp(ALIGNED), 0, 1, 130, 128, _vp(ALIGNED), _vp(ALIGNED), None) == 2
     assert L.dsmoe_quant_w_128x128(_vp(ALIGNED), 0, 1, 128, 128, None, _vp(ALIGNED), None) == 1
     assert L.dsmoe_quant_w_128x128(_vp(ALIGNED), 0, 1, 128, 128, _vp(ALIGNED), _vp(MISALIGNED), None) == 3
+    a = _vp(ALIGNED)
+    assert L.dsmoe_transpose_w_128x128(a, a, 1, 130, 128, a, a, None) == 2
+    assert L.dsmoe_transpose_w_128x128(a, a, -1, 128, 128, a, a, None) == 2
+    assert L.dsmoe_transpose_w_128x128(a, a, 1, 128, 128, None, a, None) == 1
+    assert L.dsmoe_transpose_w_128x128(a, a, 1, 128, 128, _vp(MISALIGNED), a, None) == 3
+    assert L.dsmoe_transpose_w_128x128(None, None, 0, 128, 128, None, None, None) == 0
 
 
 def test_granularity_validation_errors():
