@@ -50,9 +50,12 @@ class _Weights(ctypes.Structure):
                                    "router_w")]
 
 
+_DEBUG_BUFFERS = ("qx", "sx", "logits", "topk_idx", "gates", "offsets", "perm", "inv")
+
+
 class _Debug(ctypes.Structure):
-    _fields_ = [(n, _vp) for n in ("qx", "sx", "logits", "topk_idx", "gates", "offsets", "perm", "inv")] + \
-               [("stage_events", ctypes.POINTER(_vp))]
+    _fields_ = [(n, _vp) for n in _DEBUG_BUFFERS] + [("stage_events", ctypes.POINTER(_vp))] + \
+               [("qa", _vp), ("sa", _vp)]
 
 
 STAGE_EVENTS = 8
@@ -99,7 +102,7 @@ lib.dsmoe_moe_serving_workspace_bytes.restype = _sz
 lib.dsmoe_moe_serving_workspace_bytes.argtypes = [ctypes.POINTER(_Desc), _i64, _i32]
 lib.dsmoe_moe_forward_serving.restype = _int
 lib.dsmoe_moe_forward_serving.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Weights), _vp, _vp, _i32,
-                                          _vp, _vp, _i64, _vp, _int, _vp, _vp, _sz, ctypes.POINTER(_vp), _vp]
+                                          _vp, _vp, _i64, _vp, _int, _vp, _vp, _sz, ctypes.POINTER(_Debug), _vp]
 SERVING_STAGE_EVENTS = 5
 SERVING_STAGES = ("quant_route_permute", "gemm1_swiglu_requant", "gemm2_routed_and_shared", "combine")
 
@@ -390,6 +393,38 @@ def moe_workspace_bytes(desc: MoEDesc, T: int) -> int:
     return int(lib.dsmoe_moe_workspace_bytes(ctypes.byref(d), T))
 
 
+def _debug_buffers(desc, T, dev, debug, stage_events, n_events):
+    """(dict of device tensors or None, _Debug or None) for a forward call."""
+    dbg = None
+    dbg_c = None
+    if debug:
+        rows = T * desc.K + (T if desc.n_shared else 0)
+        dbg = {
+            "qx": torch.empty((T, desc.H), dtype=torch.uint8, device=dev),
+            "sx": torch.empty((T, desc.H // 128), dtype=torch.float32, device=dev),
+            "logits": torch.empty((T, desc.E), dtype=torch.float32, device=dev),
+            "topk_idx": torch.empty((T, desc.K), dtype=torch.int32, device=dev),
+            "gates": torch.empty((T, desc.K), dtype=torch.float32, device=dev),
+            "offsets": torch.empty((desc.E + 1,), dtype=torch.int32, device=dev),
+            "perm": torch.empty((T * desc.K,), dtype=torch.int32, device=dev),
+            "inv": torch.empty((T, desc.K), dtype=torch.int32, device=dev),
+            "qa": torch.empty((rows, desc.I), dtype=torch.uint8, device=dev),
+            "sa": torch.empty((rows, desc.I // 128), dtype=torch.float32, device=dev),
+        }
+        dbg_c = _Debug(*[dbg[n].data_ptr() for n in _DEBUG_BUFFERS])
+        dbg_c.qa = dbg["qa"].data_ptr()
+        dbg_c.sa = dbg["sa"].data_ptr()
+    if stage_events is not None:
+        if len(stage_events) != n_events:
+            raise ValueError(f"stage_events needs {n_events} handles")
+        arr = (_vp * n_events)(*stage_events)
+        if dbg_c is None:
+            dbg_c = _Debug()
+        dbg_c.stage_events = ctypes.cast(arr, ctypes.POINTER(_vp))
+        dbg_c._keep = arr
+    return dbg, dbg_c
+
+
 def moe_forward(desc: MoEDesc, weights: MoEWeights, bias: torch.Tensor, x: torch.Tensor,
                 out_dtype=torch.bfloat16, y: Optional[torch.Tensor] = None,
                 counts: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
@@ -410,29 +445,7 @@ def moe_forward(desc: MoEDesc, weights: MoEWeights, bias: torch.Tensor, x: torch
     need = moe_workspace_bytes(desc, T)
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
-    dbg = None
-    dbg_c = None
-    if debug:
-        dbg = {
-            "qx": torch.empty((T, desc.H), dtype=torch.uint8, device=dev),
-            "sx": torch.empty((T, desc.H // 128), dtype=torch.float32, device=dev),
-            "logits": torch.empty((T, desc.E), dtype=torch.float32, device=dev),
-            "topk_idx": torch.empty((T, desc.K), dtype=torch.int32, device=dev),
-            "gates": torch.empty((T, desc.K), dtype=torch.float32, device=dev),
-            "offsets": torch.empty((desc.E + 1,), dtype=torch.int32, device=dev),
-            "perm": torch.empty((T * desc.K,), dtype=torch.int32, device=dev),
-            "inv": torch.empty((T, desc.K), dtype=torch.int32, device=dev),
-        }
-        dbg_c = _Debug(*[dbg[n].data_ptr() for n in ("qx", "sx", "logits", "topk_idx", "gates",
-                                                      "offsets", "perm", "inv")])
-    if stage_events is not None:
-        if len(stage_events) != STAGE_EVENTS:
-            raise ValueError(f"stage_events needs {STAGE_EVENTS} handles")
-        arr = (_vp * STAGE_EVENTS)(*stage_events)
-        if dbg_c is None:
-            dbg_c = _Debug()
-        dbg_c.stage_events = ctypes.cast(arr, ctypes.POINTER(_vp))
-        dbg_c._keep = arr
+    dbg, dbg_c = _debug_buffers(desc, T, dev, debug, stage_events, STAGE_EVENTS)
     d = desc._c()
     wc = weights._c()
     _check(lib.dsmoe_moe_forward(ctypes.byref(d), ctypes.byref(wc), _p(bias), _p(x), T, _p(y),
@@ -502,10 +515,11 @@ def moe_forward_serving(desc: "MoEDesc", slot_weights: "MoEWeights", slot_first:
                         slot_expert: torch.Tensor, bias: torch.Tensor, x: torch.Tensor,
                         out_dtype=torch.bfloat16, y: Optional[torch.Tensor] = None,
                         counts: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                        stage_events=None):
+                        debug: bool = False, stage_events=None):
     """The layer forward over the slots of a replica plan, the shared expert
-    as one more routed group (dsmoe_moe_forward_serving).  Returns (y, counts).
-    stage_events: optional SERVING_STAGE_EVENTS raw hipEvent_t handles (ints)."""
+    as one more routed group (dsmoe_moe_forward_serving).  Returns (y, counts,
+    dbg) as moe_forward does.  stage_events: optional SERVING_STAGE_EVENTS raw
+    hipEvent_t handles (ints)."""
     _dev(x, torch.bfloat16, "x")
     _dev(bias, torch.float32, "bias")
     _dev(slot_first, torch.int32, "slot_first")
@@ -520,20 +534,15 @@ def moe_forward_serving(desc: "MoEDesc", slot_weights: "MoEWeights", slot_first:
     need = moe_serving_workspace_bytes(desc, T, S)
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
-    ev = None
-    if stage_events is not None:
-        if len(stage_events) != SERVING_STAGE_EVENTS:
-            raise ValueError(f"stage_events needs {SERVING_STAGE_EVENTS} handles")
-        ev = (_vp * SERVING_STAGE_EVENTS)(*stage_events)
+    dbg, dbg_c = _debug_buffers(desc, T, dev, debug, stage_events, SERVING_STAGE_EVENTS)
     d = desc._c()
     wc = slot_weights._c()
     _check(lib.dsmoe_moe_forward_serving(ctypes.byref(d), ctypes.byref(wc), _p(slot_first), _p(slot_expert), S,
                                          _p(bias), _p(x), T, _p(y), _dtype_code(y.dtype), _p(counts),
                                          _p(workspace), workspace.numel(),
-                                         ctypes.cast(ev, ctypes.POINTER(_vp)) if ev is not None else None,
-                                         _stream()),
+                                         ctypes.byref(dbg_c) if dbg_c is not None else None, _stream()),
            "dsmoe_moe_forward_serving")
-    return y, counts
+    return y, counts, dbg
 
 
 def update_bias(bias: torch.Tensor, counts: torch.Tensor, T: int, K: int, gamma: float = 0.001):

@@ -96,6 +96,42 @@ dsmoe_status check_desc(const dsmoe_moe_desc* d, int64_t T) {
   return DSMOE_OK;
 }
 
+// The debug buffers a caller asked for: 4-byte alignment of every pointer.
+bool debug_aligned(const dsmoe_moe_debug* dbg) {
+  if (!dbg) return true;
+  const void* dp[] = {dbg->qx, dbg->sx, dbg->logits, dbg->topk_idx, dbg->gates,
+                      dbg->offsets, dbg->perm, dbg->inv, dbg->qa, dbg->sa};
+  for (const void* p : dp)
+    if (p && !aligned(p, 4)) return false;
+  return true;
+}
+
+// Device-to-device copies of the forward's intermediates into the debug
+// buffers that are given (stream-ordered after the forward's kernels).
+hipError_t copy_debug(const dsmoe_moe_debug& dbg, const dsmoe_moe_desc& d, int64_t T,
+                      const Layout& L, uint8_t* ws, hipStream_t st) {
+  const size_t TK = static_cast<size_t>(T) * d.K;
+  const size_t rows = TK + (d.n_shared ? static_cast<size_t>(T) : 0);
+  struct Cp { void* dst; size_t off; size_t n; } cps[] = {
+      {dbg.qx, L.qx, static_cast<size_t>(T) * d.H},
+      {dbg.sx, L.sx, static_cast<size_t>(T) * (d.H / 128) * 4},
+      {dbg.logits, L.logits, static_cast<size_t>(T) * d.E * 4},
+      {dbg.topk_idx, L.topk, TK * 4},
+      {dbg.gates, L.gates, TK * 4},
+      {dbg.offsets, L.offsets, (static_cast<size_t>(d.E) + 1) * 4},
+      {dbg.perm, L.perm, TK * 4},
+      {dbg.inv, L.inv, TK * 4},
+      {dbg.qa, L.qa, rows * d.I},
+      {dbg.sa, L.sa, rows * (d.I / 128) * 4},
+  };
+  for (const Cp& c : cps)
+    if (c.dst) {
+      const hipError_t e = hipMemcpyAsync(c.dst, ws + c.off, c.n, hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return e;
+    }
+  return hipSuccess;
+}
+
 // Workspace of dsmoe_moe_forward_serving: the forward's regions, then the
 // per-row gates of routed and shared rows and the slots' group offsets.
 struct ServingLayout {
@@ -298,12 +334,7 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
   if (d->n_shared && (!aligned(w->w13_sh, 16) || !aligned(w->w2_sh, 16) ||
                       !aligned(w->s13_sh, 4) || !aligned(w->s2_sh, 4)))
     return DSMOE_ERR_ALIGN;
-  if (dbg) {
-    const void* dp[] = {dbg->qx, dbg->sx, dbg->logits, dbg->topk_idx, dbg->gates,
-                        dbg->offsets, dbg->perm, dbg->inv};
-    for (const void* p : dp)
-      if (p && !aligned(p, 4)) return DSMOE_ERR_ALIGN;
-  }
+  if (!debug_aligned(dbg)) return DSMOE_ERR_ALIGN;
   s = check_device();
   if (s != DSMOE_OK) return s;
 
@@ -429,21 +460,7 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
   DSMOE_MARK(7);
 #undef DSMOE_MARK
 
-  if (dbg) {
-    const size_t TK = static_cast<size_t>(T) * K;
-    struct Cp { void* dst; const void* src; size_t n; } cps[] = {
-        {dbg->qx, qx, static_cast<size_t>(T) * H},
-        {dbg->sx, sx, static_cast<size_t>(T) * (H / 128) * 4},
-        {dbg->logits, logits, static_cast<size_t>(T) * E * 4},
-        {dbg->topk_idx, topk, TK * 4},
-        {dbg->gates, gates, TK * 4},
-        {dbg->offsets, offsets, (static_cast<size_t>(E) + 1) * 4},
-        {dbg->perm, perm, TK * 4},
-        {dbg->inv, inv, TK * 4},
-    };
-    for (const Cp& c : cps)
-      if (c.dst) DSMOE_TRY(hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, st));
-  }
+  if (dbg) DSMOE_TRY(copy_debug(*dbg, *d, T, L, ws, st));
 #undef DSMOE_TRY
   return DSMOE_OK;
 }
@@ -624,10 +641,11 @@ dsmoe_status dsmoe_moe_forward_serving(const dsmoe_moe_desc* d, const dsmoe_moe_
                                        const int32_t* slot_first, const int32_t* slot_expert,
                                        int32_t n_slots, const float* bias, const void* x, int64_t T,
                                        void* y, int yt, int32_t* counts_out, void* workspace,
-                                       size_t ws_bytes, void* const* stage_events, void* stream) {
+                                       size_t ws_bytes, const dsmoe_moe_debug* dbg, void* stream) {
   dsmoe_status s = check_desc(d, T);
   if (s != DSMOE_OK) return s;
   if (!valid_dtype(yt)) return DSMOE_ERR_DTYPE;
+  void* const* stage_events = dbg ? dbg->stage_events : nullptr;
   if (stage_events)
     for (int i = 0; i < DSMOE_SERVING_STAGE_EVENTS; ++i)
       if (!stage_events[i]) return DSMOE_ERR_NULL;
@@ -644,7 +662,8 @@ dsmoe_status dsmoe_moe_forward_serving(const dsmoe_moe_desc* d, const dsmoe_moe_
   if ((x && !aligned(x, 16)) || (y && !aligned(y, 16)) || !aligned(w->w13, 16) ||
       !aligned(w->w2, 16) || !aligned(w->router_w, 16) || !aligned(w->s13, 4) ||
       !aligned(w->s2, 4) || !aligned(bias, 4) || !aligned(counts_out, 4) ||
-      !aligned(slot_first, 4) || !aligned(slot_expert, 4) || (workspace && !aligned(workspace, 256)))
+      !aligned(slot_first, 4) || !aligned(slot_expert, 4) || (workspace && !aligned(workspace, 256)) ||
+      !debug_aligned(dbg))
     return DSMOE_ERR_ALIGN;
   if (d->n_shared && (!aligned(w->w13_sh, 16) || !aligned(w->w2_sh, 16) ||
                       !aligned(w->s13_sh, 4) || !aligned(w->s2_sh, 4)))
@@ -747,6 +766,7 @@ dsmoe_status dsmoe_moe_forward_serving(const dsmoe_moe_desc* d, const dsmoe_moe_
   DSMOE_TRY(dsmoe::launch_combine(o, inv, T, K, H, sh ? TK : -1, y, yt == DSMOE_F32, st));
   DSMOE_MARK(4);
 #undef DSMOE_MARK
+  if (dbg) DSMOE_TRY(copy_debug(*dbg, *d, T, L, ws, st));
 #undef DSMOE_TRY
   return DSMOE_OK;
 }

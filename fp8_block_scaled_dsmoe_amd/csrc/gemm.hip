@@ -235,9 +235,9 @@ __device__ __forceinline__ void epi_rows(const GemmProblem& p, const f32x4 (&acc
 // over its 128 columns is reduced in registers (16 lanes, DPP) and across
 // the NSLOTS waves that share the row through s_rmax by one thread per row,
 // which also forms scale = amax / 448 (IEEE division), stores it and leaves
-// 1 / scale for the code pass: code = E4M3(a * (1 / scale)), within an ulp
-// of a / scale, by the hardware conversion.  The codes are stored with
-// 16-byte writes.
+// it for the code pass: code = E4M3(a / scale) from the IEEE quotient, as in
+// the standalone quantisers, by the hardware conversion.  The codes are
+// stored with 16-byte writes.
 //   s_ex:   [pairs][2][NI][NJ/2][64 lanes] f32x4
 //   s_rmax: [NSLOTS][ROWS] f32
 //   s_code: [ROWS][128] bytes
@@ -293,14 +293,14 @@ __device__ __forceinline__ void epi_swiglu(const GemmProblem& p, const f32x4 (&a
   }
   __syncthreads();
   const int64_t I = p.N / 2;
-  // one thread per row: the row's scale (stored) and its reciprocal, left in
-  // slot 0 of s_rmax (each thread reads and writes only its own row)
+  // one thread per row: the row's scale, stored and left in slot 0 of
+  // s_rmax (each thread reads and writes only its own row)
   for (int lr = threadIdx.x; lr < ROWS; lr += blockDim.x) {
     float amax = s_rmax[lr];
 #pragma unroll
     for (int w = 1; w < NSLOTS; ++w) amax = fmaxf(amax, s_rmax[w * ROWS + lr]);
     const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
-    s_rmax[lr] = 1.0f / sc;
+    s_rmax[lr] = sc;
     const int64_t row = row0 + lr;
     if (row < row1) p.c_scale[row * (I / BK) + nt] = sc;
   }
@@ -311,10 +311,10 @@ __device__ __forceinline__ void epi_swiglu(const GemmProblem& p, const f32x4 (&a
 #pragma unroll
     for (int r = 0; r < 4; r += 2) {   // rows lr, lr + 1: one packed conversion
       const int lr = row_base + i * 16 + (lane >> 4) * 4 + r;
-      const float rs0 = s_rmax[lr], rs1 = s_rmax[lr + 1];
+      const float sc0 = s_rmax[lr], sc1 = s_rmax[lr + 1];
 #pragma unroll
       for (int j = 0; j < HJ; ++j) {
-        const uint32_t c2 = e4m3_encode2(av[i][j][r] * rs0, av[i][j][r + 1] * rs1);
+        const uint32_t c2 = e4m3_encode2(av[i][j][r] / sc0, av[i][j][r + 1] / sc1);
         s_code[lr * 128 + ccol + j * 16] = static_cast<uint8_t>(c2);
         s_code[(lr + 1) * 128 + ccol + j * 16] = static_cast<uint8_t>(c2 >> 8);
       }

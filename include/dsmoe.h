@@ -222,13 +222,18 @@ typedef struct dsmoe_moe_weights {
  * Optional device buffers that receive the layer's intermediates (each
  * pointer may be NULL):  qx [T][H] and sx [T][H/128] (the 1x128 codes of x),
  * logits [T][E], topk_idx and gates [T][K], offsets [E+1], perm [T*K],
- * inv [T][K].
- * stage_events (host array, may be NULL): DSMOE_STAGE_EVENTS hipEvent_t
- * handles (passed as void*) created by the caller; event 0 is recorded on
- * the stream before the first kernel and event i after stage i:
- * 1 quantise x, 2 router logits, 3 top-K selection, 4 permute,
- * 5 gate/up GEMM + SwiGLU + requant, 6 routed down GEMM,
- * 7 shared down GEMM + combine.  Recording them changes no result.
+ * inv [T][K], and the down projections' FP8 input: qa [T*K + n_shared*T][I]
+ * codes and sa [T*K + n_shared*T][I/128] scales of the requantised SwiGLU
+ * output a (V3 notes §6.1), one row per (token, routed expert) pair in the
+ * order of perm (row inv[t][k] is token t's k-th expert), then, with a
+ * shared expert, row T*K + t for token t.
+ * stage_events (host array, may be NULL): hipEvent_t handles (passed as
+ * void*) created by the caller, recorded on the stream.  dsmoe_moe_forward
+ * takes DSMOE_STAGE_EVENTS of them: event 0 before the first kernel and
+ * event i after stage i: 1 quantise x, 2 router logits, 3 top-K selection,
+ * 4 permute, 5 gate/up GEMM + SwiGLU + requant, 6 routed down GEMM,
+ * 7 shared down GEMM + combine.  dsmoe_moe_forward_serving takes
+ * DSMOE_SERVING_STAGE_EVENTS (see there).  Recording them changes no result.
  */
 #define DSMOE_STAGE_EVENTS 8
 typedef struct dsmoe_moe_debug {
@@ -241,6 +246,8 @@ typedef struct dsmoe_moe_debug {
   int32_t* perm;
   int32_t* inv;
   void* const* stage_events;
+  uint8_t* qa;
+  float* sa;
 } dsmoe_moe_debug;
 
 /* Bytes of device workspace dsmoe_moe_forward needs for T tokens
@@ -373,11 +380,13 @@ size_t dsmoe_moe_serving_workspace_bytes(const dsmoe_moe_desc* d, int64_t T, int
  *                dsmoe_place_replicas from the per-expert weights
  *   slot_first   [E+1], slot_expert [n_slots] int32: the plan the slots were
  *                placed with (slot_first[E] must equal n_slots)
- *   stage_events NULL, or DSMOE_SERVING_STAGE_EVENTS hipEvent_t (created by
- *                the caller) recorded on `stream` at the start, after the
- *                permute, after the gate/up launch, after the down launch and
- *                after the combine
- *   everything else as in dsmoe_moe_forward (no debug copies)
+ *   dbg          NULL, or a dsmoe_moe_debug whose buffers receive the same
+ *                intermediates as in dsmoe_moe_forward (qa/sa in the same
+ *                row order: the slots only refine the group offsets); its
+ *                stage_events, if given, are DSMOE_SERVING_STAGE_EVENTS
+ *                handles recorded at the start, after the permute, after the
+ *                gate/up launch, after the down launch and after the combine
+ *   everything else as in dsmoe_moe_forward
  * Routing, gates and counts_out (per expert) are those of dsmoe_moe_forward.
  * The rows of expert e (its tokens, ascending) are cut into its n_e slots in
  * contiguous chunks: slot slot_first[e] + j starts at row offsets[e] +
@@ -394,7 +403,7 @@ dsmoe_status dsmoe_moe_forward_serving(const dsmoe_moe_desc* d, const dsmoe_moe_
                                        const int32_t* slot_first, const int32_t* slot_expert,
                                        int32_t n_slots, const float* bias, const void* x, int64_t T,
                                        void* y, int yt, int32_t* counts_out, void* workspace,
-                                       size_t ws_bytes, void* const* stage_events, void* stream);
+                                       size_t ws_bytes, const dsmoe_moe_debug* dbg, void* stream);
 
 /*
  * Coarser scaling granularities, for comparison with the recipe's 1x128 /

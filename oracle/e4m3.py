@@ -67,11 +67,25 @@ def decode(codes: np.ndarray) -> np.ndarray:
     return _DECODE_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
+_CHUNK = 1 << 16     # elements per pass (keeps the temporaries in cache)
+
+
 def encode(values: np.ndarray) -> np.ndarray:
     """Vectorised encode of float32 values to uint8 codes.
 
     Same steps as encode_scalar, on whole arrays; np.rint rounds half to even.
+    The elements are taken in slices of _CHUNK (each element independently,
+    so the slicing changes no code; it only keeps the temporaries small).
     """
+    v = np.asarray(values, dtype=np.float32)
+    flat = v.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for i in range(0, flat.size, _CHUNK):
+        out[i:i + _CHUNK] = _encode_slice(flat[i:i + _CHUNK])
+    return out.reshape(v.shape)
+
+
+def _encode_slice(values: np.ndarray) -> np.ndarray:
     v = np.asarray(values, dtype=np.float32).astype(np.float64)
     sign = np.where(np.signbit(v), 0x80, 0x00).astype(np.int64)
     a = np.abs(v)

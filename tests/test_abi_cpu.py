@@ -144,7 +144,12 @@ def test_serving_validation_errors():
     assert F(byref(dc), byref(wc), a, a, 20, a, a, 256, a, 0, a, a, ws - 1, None, None) == 5
     assert F(byref(dc), byref(wc), a, a, 20, a, a, 256, a, 9, a, a, ws, None, None) == 4
     null_events = (ctypes.c_void_p * 5)()
-    assert F(byref(dc), byref(wc), a, a, 20, a, a, 256, a, 0, a, a, ws, null_events, None) == 1
+    dbg = d._Debug()
+    dbg.stage_events = ctypes.cast(null_events, ctypes.POINTER(ctypes.c_void_p))
+    assert F(byref(dc), byref(wc), a, a, 20, a, a, 256, a, 0, a, a, ws, byref(dbg), None) == 1
+    dbg = d._Debug()
+    dbg.qa = MISALIGNED                                                            # debug buffers 4-byte aligned
+    assert F(byref(dc), byref(wc), a, a, 20, a, a, 256, a, 0, a, a, ws, byref(dbg), None) == 3
 
 
 def test_route_and_bias_validation_errors():

@@ -12,6 +12,7 @@
 import math
 
 import numpy as np
+import pytest
 
 from oracle import e4m3, layer, quant
 from dsmoe_inputs import LayerConfig, layer_inputs_host, normal_bf16
@@ -136,28 +137,62 @@ def test_zero_input_gives_zero_output():
     assert out["counts"].sum() == cfg.T * cfg.K
 
 
-def test_requant_slack_flags_codes_at_midpoints_only():
+def test_requant_ambiguity_flags_codes_at_midpoints_only():
     # one 128-wide tile with amax 448 (scale 1): 17 sits on the 16/18 midpoint,
-    # 16 is a code value, 17.5 is a quarter step from every midpoint
+    # 16 is a code value, 17.5 is half a step from both of its midpoints
     a = np.zeros((1, 128), np.float32)
     a[0, :4] = [448.0, 17.0, 16.0, 17.5]
     qa, sa = quant.quant_act_1x128(a)
     assert sa[0, 0] == 1.0
     h = np.zeros((1, 256))
     h_d = np.zeros((1, 256))
-    w2 = np.zeros((128, 128), np.float32)
-    w2[:, 1] = 0.5
-    w2[:, 2] = 0.25
-    w2[:, 3] = 0.125
-    w2[0, 0] = 448.0 * 2.0 ** -10          # sets every block scale to 2^-10
-    q2, s2 = quant.quant_w_128x128(w2)
-    slack, n_amb = layer.requant_slack(h, h_d, a, qa, sa, q2, s2, 0.0)
-    assert n_amb == 1
-    # only column 1 counts: step of code 16 is max(16-15, 18-16) = 2
-    assert np.allclose(slack[0], 2 * np.abs(w2[:, 1]))
-    # a large error bound makes every non-zero element ambiguous
-    _, n_all = layer.requant_slack(h + 1.0, np.ones((1, 256)) * 1e3, a, qa, sa, q2, s2, 1.0)
-    assert n_all == 128
+    amb, lo, hi, sa_tol = layer.requant_ambiguity(h, h_d, a, qa, sa, 0.0)
+    assert amb.sum() == 1 and amb[0, 1]
+    assert (lo[0, 1], hi[0, 1]) == (16.0, 18.0)
+    assert (lo[0, 2], hi[0, 2]) == (16.0, 16.0) and (lo[0, 3], hi[0, 3]) == (18.0, 18.0)
+    assert (lo[0, 0], hi[0, 0]) == (448.0, 448.0) and np.all(lo[0, 4:] == 0) and np.all(hi[0, 4:] == 0)
+    # with no error in h the scale may move only by the float32 evaluation of
+    # a (8 ulps of the amax, over 448) and one ulp of the division
+    assert sa_tol[0, 0] == 8 * 2.0 ** -24 + 2.0 ** -23
+    # a large error bound makes every element ambiguous, zeros included, over
+    # the whole code range
+    amb_all, lo_all, hi_all, _ = layer.requant_ambiguity(h + 1.0, np.ones((1, 256)) * 1e3, a, qa, sa, 1.0)
+    assert amb_all.sum() == 128 and np.all(lo_all == -448.0) and np.all(hi_all == 448.0)
+
+
+@pytest.mark.parametrize("rel", [2e-5, 5e-4])
+def test_requant_ambiguity_covers_perturbed_implementations(rel):
+    # An implementation whose h is off by up to rel * h_d (here every element
+    # pushed almost to the bound with a random sign) and which evaluates silu(g) * u
+    # in float32 must land on a code inside the valid range everywhere (the
+    # oracle's code wherever the range is one code), and within sa_tol on the
+    # scales.  The larger error moves small values by several codes.
+    H, I, n = 512, 256, 400
+    x = normal_bf16("amb_x", (n, H), 1.0, seed=6)
+    w13 = normal_bf16("amb_w13", (2 * I, H), 0.02, seed=6)
+    qx, sx = quant.quant_act_1x128(x)
+    q13, s13 = quant.quant_w_128x128(w13)
+    h, a32, qa, sa = layer.expert_gate_up(qx, sx, q13, s13)
+    from oracle.gemm import gemm_normaliser
+    h_d = gemm_normaliser(qx, sx, q13, s13)
+    amb, lo, hi, sa_tol = layer.requant_ambiguity(h, h_d, a32, qa, sa, rel)
+    # (0.999: room for the float32 rounding of the perturbed h itself)
+    sign = np.where(np.random.default_rng(1).random(h.shape) < 0.5, -1.0, 1.0)
+    hp = (h + sign * 0.999 * rel * h_d).astype(np.float32)
+    g, u = hp[:, :I], hp[:, I:]
+    with np.errstate(over="ignore"):
+        ap = (g / (np.float32(1) + np.exp(-g)) * u).astype(np.float32)
+    qp, sp = quant.quant_act_1x128(ap)
+    vp = e4m3.decode(qp)
+    differ = vp != e4m3.decode(qa)
+    assert differ.sum() > 0, "the perturbation should move some codes"
+    assert np.all((vp >= lo) & (vp <= hi)), "a code moved outside its valid range"
+    assert not np.any(differ & ~amb), "a code moved that is not flagged"
+    assert np.all(np.abs(sp.astype(np.float64) - sa) <= sa_tol)
+    # the bound is relative to |x_hat| . |w13_hat| (h itself cancels), so it
+    # flags more codes than move, but at the FP32 bound still a small share
+    if rel < 1e-4:
+        assert amb.mean() < 0.1
 
 
 def test_router_logits_one_hot_rows_pick_router_columns():
