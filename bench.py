@@ -1,6 +1,13 @@
 """Benchmark of the DeepSeekMoE FP8 layer forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload v3_prefill]
+    python bench.py [--steps K] [--warmup W] [--workload v3_skew]
+
+The default workload is the largest configuration: the DeepSeek-V3-shaped
+layer on T = 32768 tokens whose expert popularity follows Zipf(1.1) (v3_skew).
+It also reports the load imbalance before and after one bias update of the
+aux-loss-free balancing (and re-route), and, outside the timed region, the
+imbalance along a routing-only run of many updates.  v3_prefill (T = 4096)
+and v3_decode (T = 64) are the other layer workloads.
 
 The dense workload (--workload c2_dense) times one block-scaled FP8 GEMM
 instead: A [4096][7168] and B [7168][4096] (passed as W [4096][7168]) from the
@@ -67,14 +74,18 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="v3_prefill",
+    ap.add_argument("--workload", default="v3_skew",
                     choices=["v3_prefill", "v3_decode", "v3_skew", "tiny", "c2_dense", "c2_granularity",
                              "v3_decode_serving", "v3_prefill_dgrad"])
     ap.add_argument("--extra-slots", type=int, default=64,
                     help="v3_decode_serving: copies of hot experts beyond one slot per expert")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=14)
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="tokens of the batch the CPU oracle runs (default: 64 for v3_skew, whose tokens "
+                         "share few experts, else 14; about 10 s of oracle work either way)")
+    ap.add_argument("--balance-steps", type=int, default=1000,
+                    help="layer workloads: routing-only bias updates for the imbalance trajectory (0: none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times): the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -82,8 +93,8 @@ def parse():
 
 
 COPY_BYTES = 1 << 30
-def traffic_file(workload):
-    return os.path.join(ROOT, "profiles", f"traffic_gemm1_swiglu_{workload}.json")
+def counters_file(workload):
+    return os.path.join(ROOT, "profiles", f"counters_gemm1_swiglu_{workload}.json")
 GEMM_SOURCES = ["gemm.hip", "common.h", "gemm.h"]
 
 
@@ -96,17 +107,53 @@ def gemm_sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the gate/up GEMM from the committed counter runs,
-    or None when they were taken on other kernel sources or another workload."""
+def gemm1_counters(workload):
+    """The committed rocprofv3 counter record of the gate/up launch for this
+    workload, or None when it was taken on other GEMM sources."""
     try:
-        with open(traffic_file(workload)) as fh:
+        with open(counters_file(workload)) as fh:
             t = json.load(fh)
     except OSError:
         return None
     if t.get("workload") != workload or t.get("gemm_sources_sha256") != gemm_sources_sha256():
         return None
-    return int(t["traffic_bytes_per_launch"])
+    return t
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the gate/up GEMM (reads from the per-size TCC
+    read-request counters, writes from the write-request counters), or None."""
+    t = gemm1_counters(workload)
+    return None if t is None or "traffic_bytes_per_launch" not in t else int(t["traffic_bytes_per_launch"])
+
+
+def measured_mfma(workload):
+    """MFMA busy fraction of the gate/up launch from the counter record, or None."""
+    t = gemm1_counters(workload)
+    return None if t is None or "mfma_busy_frac" not in t else t["mfma_busy_frac"]
+
+
+def host_info():
+    """CPU model and the BLAS NumPy uses (name, version, threads)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+                break
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas}
 
 
 def copy_calibration(torch):
@@ -154,6 +201,31 @@ def build_layer(cfg, d, torch, dsi):
     return x, bias, weights, statistics.median(times)
 
 
+def imbalance(counts):
+    """Load-balance figures of one routing: max/mean and coefficient of
+    variation of the per-expert loads, experts with no load."""
+    import numpy as np
+    c = np.asarray(counts, np.float64)
+    return {"max_over_mean": round(float(c.max() / c.mean()), 3),
+            "cv": round(float(c.std() / c.mean()), 3),
+            "zero_load_experts": int((c == 0).sum())}
+
+
+def routing_trajectory(d, torch, logits, bias_init, cfg, n_steps):
+    """Imbalance along n_steps aux-loss-free bias updates with routing only
+    (dsmoe_route + dsmoe_update_bias on the batch's fixed logits), at a few
+    step counts; untimed."""
+    bias = bias_init.clone()
+    marks = sorted({m for m in (0, 1, 10, 100, 300, 1000, 3000, n_steps) if m <= n_steps})
+    out = {}
+    for i in range(n_steps + 1):
+        r = d.route(logits, bias, cfg.G, cfg.Mg, cfg.K)
+        if i in marks:
+            out[str(i)] = imbalance(r["counts"].cpu().numpy())
+        d.update_bias(bias, r["counts"], cfg.T, cfg.K, 0.001)
+    return out
+
+
 def cpu_baseline(cfg, n_tokens, torch, dsi):
     """The oracle, as it stands, on a bounded sample: n_tokens tokens of the
     same batch through the whole layer (weight quantisation excluded, as on
@@ -194,7 +266,7 @@ def cpu_baseline(cfg, n_tokens, torch, dsi):
     ol.moe_layer(xs, inp["router_w"], inp["bias"], lambda e: cache[e], cache[cfg.E], cfg.G, cfg.Mg, cfg.K)
     dt = time.perf_counter() - t0
     return {
-        "value": n_tokens / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+        "value": n_tokens / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle", **host_info(),
         "sample": f"{n_tokens} tokens of the {cfg.name} batch through the whole layer "
                   f"({len(needed)} experts incl. shared; float64 NumPy; weight quantisation excluded), "
                   f"{dt:.1f} s",
@@ -217,7 +289,7 @@ def dense_cpu_baseline(a, w, n_rows):
     og.block_scaled_gemm(qa, sa, qw, sw)
     dt = time.perf_counter() - t0
     flops = 2.0 * n_rows * w.shape[0] * w.shape[1]
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle", **host_info(),
             "sample": f"the first {n_rows} rows of A through the oracle GEMM (float64 NumPy, "
                       f"quantisation excluded), {dt:.1f} s"}
 
@@ -313,7 +385,7 @@ def granularity_cpu_baseline(a, w, n_rows):
     ah @ wh.T
     dt = time.perf_counter() - t0
     flops = 2.0 * n_rows * w.shape[0] * w.shape[1]
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle", **host_info(),
             "sample": f"the first {n_rows} rows of A through the oracle's block-granularity path "
                       f"(quantisation of the A rows and all of W included; float64 NumPy), {dt:.1f} s"}
 
@@ -570,7 +642,7 @@ def run_serving(args, torch):
         "placement_gbps": round(place_bytes / (place_ms * 1e-3) / 1e9, 1),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens, torch, dsi)
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens or 14, torch, dsi)
         result["cpu_baseline"]["sample"] += " (the serving forward computes the same layer)"
     print(json.dumps(result), flush=True)
 
@@ -698,10 +770,27 @@ def main():
                       stage_events=None if ev is None else [e.cuda_event for e in ev])
         d.update_bias(bias, counts, T, K, 0.001)
 
+    # Load balance: the routing of the batch with the initial bias, then one
+    # bias update (the step's own) and the re-route.
+    import numpy as np
+    bias_init = bias.clone()
+    _, _, dbg0 = d.moe_forward(desc, weights, bias, x, y=y, counts=counts, workspace=ws, debug=True)
+    counts_before = counts.cpu().numpy()
+    d.update_bias(bias, counts, T, K, 0.001)
+    d.moe_forward(desc, weights, bias, x, y=y, counts=counts, workspace=ws)
+    counts_after1 = counts.cpu().numpy()
+    bias.copy_(bias_init)
+    balance = {"before": imbalance(counts_before), "after_one_update": imbalance(counts_after1)}
+    if args.balance_steps > 0:
+        balance["routing_only_trajectory"] = routing_trajectory(d, torch, dbg0["logits"], bias_init, cfg,
+                                                                args.balance_steps)
+    del dbg0
+    log("load imbalance (max/mean): before " + f"{balance['before']['max_over_mean']:.3f}, after one update "
+        f"{balance['after_one_update']['max_over_mean']:.3f}")
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    counts_first = counts.cpu().numpy()
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(d.STAGE_EVENTS)] for _ in range(args.steps)]
     for row in ev:
@@ -723,7 +812,6 @@ def main():
     log(f"{args.steps} steps: {ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}); stages " +
         ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
 
-    import numpy as np
     counts_last = counts.cpu().numpy()
     touched = int(np.count_nonzero(counts_last))
     rows1 = T * K + T
@@ -761,11 +849,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: DeepSeekMoE layer forward + bias update, T={T}, H={H}, "
                                f"E={E} in G={cfg.G} groups, top-{K} within {cfg.Mg} groups, "
-                               f"1 shared expert, I={I}, y {args.out_dtype}",
+                               f"1 shared expert, I={I}, y {args.out_dtype}" +
+                               (f", expert popularity Zipf({cfg.zipf_s}) through the router logits"
+                                if cfg.zipf_s else ""),
                    "T": T, "H": H, "E": E, "G": cfg.G, "Mg": cfg.Mg, "K": K, "I": I},
         "roofline": {"bound": g1_bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(cfg.name),
+                     "mfma_busy_frac": measured_mfma(cfg.name),
                      "kernel": "gate/up grouped FP8 GEMM + SwiGLU + 1x128 requant (one launch)",
                      "algorithmic_bytes": int(g1_bytes), "algorithmic_flops": g1_flops,
                      "avg_ms": round(g1_ms, 4)},
@@ -779,12 +870,11 @@ def main():
         "experts_touched": touched,
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "quant_w_ms": round(quant_w_ms, 3),
-        "load_imbalance": {"max_over_mean_first": round(float(counts_first.max() / counts_first.mean()), 3),
-                           "max_over_mean_last": round(float(counts_last.max() / counts_last.mean()), 3),
-                           "zero_load_experts_last": int((counts_last == 0).sum())},
+        "load_balance": dict(balance, last_timed_step=imbalance(counts_last)),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens, torch, dsi)
+        n_cpu = args.cpu_tokens if args.cpu_tokens is not None else (64 if cfg.zipf_s else 14)
+        result["cpu_baseline"] = cpu_baseline(cfg, n_cpu, torch, dsi)
     print(json.dumps(result), flush=True)
 
 
