@@ -80,6 +80,10 @@ lib.dsmoe_moe_workspace_bytes.argtypes = [ctypes.POINTER(_Desc), _i64]
 lib.dsmoe_moe_forward.restype = _int
 lib.dsmoe_moe_forward.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Weights), _vp, _vp, _i64, _vp,
                                   _int, _vp, _vp, _sz, ctypes.POINTER(_Debug), _vp]
+lib.dsmoe_moe_forward_noalloc.restype = _int
+lib.dsmoe_moe_forward_noalloc.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Weights), _vp, _vp, _i64, _vp,
+                                          _int, _vp, ctypes.POINTER(_Debug), _vp]
+NOALLOC_SCRATCH_BYTES = 80 << 20
 lib.dsmoe_update_bias.restype = _int
 lib.dsmoe_update_bias.argtypes = [_vp, _vp, _i32, _i64, _i32, ctypes.c_float, _vp]
 lib.dsmoe_quant_rows.restype = _int
@@ -111,7 +115,7 @@ EXPORTED = ("dsmoe_status_str", "dsmoe_abi_version", "dsmoe_quant_act_1x128", "d
             "dsmoe_update_bias", "dsmoe_quant_rows", "dsmoe_quant_tensor",
             "dsmoe_gemm_granularity_workspace_bytes", "dsmoe_fp8_gemm_granularity",
             "dsmoe_plan_replicas", "dsmoe_place_replicas", "dsmoe_slot_offsets", "dsmoe_moe_serving_workspace_bytes",
-            "dsmoe_moe_forward_serving", "dsmoe_transpose_w_128x128")
+            "dsmoe_moe_forward_serving", "dsmoe_transpose_w_128x128", "dsmoe_moe_forward_noalloc")
 
 # dsmoe_granularity codes
 GRANULARITIES = {"tensor": 0, "channel": 1, "block": 2}
@@ -452,6 +456,31 @@ def moe_forward(desc: MoEDesc, weights: MoEWeights, bias: torch.Tensor, x: torch
                                  _dtype_code(y.dtype), _p(counts), _p(workspace), workspace.numel(),
                                  ctypes.byref(dbg_c) if dbg_c is not None else None, _stream()),
            "dsmoe_moe_forward")
+    return y, counts, dbg
+
+
+def moe_forward_noalloc(desc: MoEDesc, weights: MoEWeights, bias: torch.Tensor, x: torch.Tensor,
+                        out_dtype=torch.bfloat16, y: Optional[torch.Tensor] = None,
+                        counts: Optional[torch.Tensor] = None, debug: bool = False, stage_events=None):
+    """The layer forward on the library's own device scratch
+    (dsmoe_moe_forward_noalloc): no workspace; with y and counts given, the
+    call allocates nothing.  Returns (y, counts, dbg) as moe_forward does."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(bias, torch.float32, "bias")
+    _dev(weights.router_w, torch.bfloat16, "router_w")
+    T = x.shape[0]
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, desc.H), dtype=out_dtype, device=dev)
+    if counts is None:
+        counts = torch.empty((desc.E,), dtype=torch.int32, device=dev)
+    dbg, dbg_c = _debug_buffers(desc, T, dev, debug, stage_events, STAGE_EVENTS)
+    d = desc._c()
+    wc = weights._c()
+    _check(lib.dsmoe_moe_forward_noalloc(ctypes.byref(d), ctypes.byref(wc), _p(bias), _p(x), T, _p(y),
+                                         _dtype_code(y.dtype), _p(counts),
+                                         ctypes.byref(dbg_c) if dbg_c is not None else None, _stream()),
+           "dsmoe_moe_forward_noalloc")
     return y, counts, dbg
 
 

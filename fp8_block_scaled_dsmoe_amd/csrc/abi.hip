@@ -5,9 +5,18 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "dsmoe.h"
 #include "kernels.h"
+
+// Scratch of dsmoe_moe_forward_noalloc: one array per GPU, part of the
+// library's device code, so no call allocates.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): its device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept in g_scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[DSMOE_NOALLOC_SCRATCH_BYTES];
+
 
 namespace {
 
@@ -19,6 +28,24 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 dsmoe_status launch_status(hipError_t e) { return e == hipSuccess ? DSMOE_OK : DSMOE_ERR_LAUNCH; }
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[64];
+
+// The current device's address of `scratch`, or nullptr on failure.
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 // Device check, cached per device ordinal (idempotent).
 std::atomic<int> g_dev_ok[64];
@@ -463,6 +490,20 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
   if (dbg) DSMOE_TRY(copy_debug(*dbg, *d, T, L, ws, st));
 #undef DSMOE_TRY
   return DSMOE_OK;
+}
+
+dsmoe_status dsmoe_moe_forward_noalloc(const dsmoe_moe_desc* d, const dsmoe_moe_weights* w,
+                                       const float* bias, const void* x, int64_t T, void* y, int yt,
+                                       int32_t* counts_out, const dsmoe_moe_debug* dbg, void* stream) {
+  const dsmoe_status s = check_desc(d, T);
+  if (s != DSMOE_OK) return s;
+  if (layout_for(*d, T).total > DSMOE_NOALLOC_SCRATCH_BYTES) return DSMOE_ERR_WORKSPACE;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  void* ws = scratch_for_current_device();
+  if (!ws) return DSMOE_ERR_DEVICE;
+  return dsmoe_moe_forward(d, w, bias, x, T, y, yt, counts_out, ws, DSMOE_NOALLOC_SCRATCH_BYTES, dbg,
+                           stream);
 }
 
 dsmoe_status dsmoe_update_bias(float* bias, const int32_t* counts, int32_t E, int64_t T,

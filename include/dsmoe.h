@@ -287,6 +287,26 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
                                const dsmoe_moe_debug* dbg, void* stream);
 
 /*
+ * dsmoe_moe_forward_noalloc -- dsmoe_moe_forward without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The forward's scratch is a device array inside the library of
+ * DSMOE_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held until the process
+ * ends; it covers the DeepSeek-V3 shapes (H 7168, I 2048, E 256, K 8) up to
+ * T = 256 tokens (dsmoe_moe_workspace_bytes gives the need of a call).
+ * Arguments and results as in dsmoe_moe_forward.  Returns
+ * DSMOE_ERR_WORKSPACE, with nothing enqueued, when the call needs more than
+ * that.  The call allocates nothing.  Every call on a GPU shares that GPU's
+ * array (the forward reads no scratch content it did not write in the same
+ * call): calls that overlap on one GPU (on different streams, or from
+ * several threads) race and must be serialised by the caller.
+ */
+#define DSMOE_NOALLOC_SCRATCH_BYTES (80ull << 20)
+dsmoe_status dsmoe_moe_forward_noalloc(const dsmoe_moe_desc* d, const dsmoe_moe_weights* w,
+                                       const float* bias, const void* x, int64_t T, void* y, int yt,
+                                       int32_t* counts_out, const dsmoe_moe_debug* dbg, void* stream);
+
+/*
  * dsmoe_update_bias -- auxiliary-loss-free bias update.
  * Source: V3 notes §4 (after each step an overloaded expert's bias is
  * lowered and an underloaded expert's raised), §4.1 (speed gamma = 0.001);

@@ -20,7 +20,7 @@ def _declared():
 def test_library_exports_every_declared_function():
     import fp8_block_scaled_dsmoe_amd as d
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(d.lib, n), f"{n} not exported"
     assert sorted(d.EXPORTED) == names
@@ -201,6 +201,24 @@ def test_moe_forward_validation_errors():
     assert call({"d": ctypes.byref(bad)}) == 2
     w_null = d._Weights(*([ALIGNED] * 4 + [None] + [ALIGNED] * 4))
     assert call({"w": ctypes.byref(w_null)}) == 1
+
+
+def test_noalloc_forward_rejects_calls_beyond_its_scratch():
+    """dsmoe_moe_forward_noalloc runs on a fixed device array: the V3 shapes
+    fit up to T = 256 tokens; larger calls are refused before anything is
+    enqueued (checked on the host, no device touched)."""
+    import fp8_block_scaled_dsmoe_amd as d
+    L = d.lib
+    desc = d._Desc(7168, 2048, 256, 8, 4, 8, 1)
+    assert L.dsmoe_moe_workspace_bytes(ctypes.byref(desc), 256) <= d.NOALLOC_SCRATCH_BYTES
+    assert L.dsmoe_moe_workspace_bytes(ctypes.byref(desc), 300) > d.NOALLOC_SCRATCH_BYTES
+    w = d._Weights(*([ALIGNED] * 9))
+    a = _vp(ALIGNED)
+    F = L.dsmoe_moe_forward_noalloc
+    assert F(ctypes.byref(desc), ctypes.byref(w), a, a, 300, a, 0, a, None, None) == 5      # DSMOE_ERR_WORKSPACE
+    assert F(ctypes.byref(desc), ctypes.byref(w), a, a, 4096, a, 0, a, None, None) == 5
+    bad = d._Desc(7168, 2048, 256, 8, 4, 8, 2)
+    assert F(ctypes.byref(bad), ctypes.byref(w), a, a, 64, a, 0, a, None, None) == 2
 
 
 C_PROGRAM = r"""
