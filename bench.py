@@ -22,14 +22,16 @@ decode batch (T=64) through dsmoe_moe_forward_serving: the shared expert as a
 placed once before timing.  A step is the serving forward plus the bias
 update; the plain decode step is timed in the same process for comparison.
 
-The data-gradient workload (--workload v3_prefill_dgrad) times the FP8
-dgrad GEMMs of the routed experts at V3 prefill size on the batch's own
-routing: the block transposes of W2 and W13 (dsmoe_transpose_w_128x128), then
-dA = dy . W2 over the permuted rows (dy quantised 1x128 along H, rows gathered
-by token) and dx_rows = dh . W13 (dh quantised 1x128 along 2I), both with
-dsmoe_fp8_grouped_gemm on the transposed weights.  dy and dh are seeded
-N(0, 1) bf16 stand-ins: the SwiGLU backward that would produce dh is not part
-of it.
+The backward workload (--workload v3_prefill_backward) times the FP8
+backward of the routed experts and the shared one at V3 prefill size on the
+forward's own intermediates (routing, x codes, codes of a): h and the
+ungated expert outputs recomputed by the grouped GEMM, the gate and
+router-logit gradients, the dgrad of the down projection on the
+block-transposed W2, the SwiGLU backward (recomputing a), the dgrad of the
+gate/up projection summed per token, and the weight gradients of W2 and W13
+on 1x128 tiles along each expert's tokens.  dy ~ N(0, 1) stands in for the
+loss gradient.  The weights' block transposes run once per weight version
+and are timed apart.
 
 The granularity workload (--workload c2_granularity) runs the same GEMM
 end to end from the bf16 operands at three scaling granularities (one scale
@@ -76,10 +78,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="v3_skew",
                     choices=["v3_prefill", "v3_decode", "v3_skew", "tiny", "c2_dense", "c2_granularity",
-                             "v3_decode_serving", "v3_prefill_dgrad"])
+                             "v3_decode_serving", "v3_prefill_backward"])
     ap.add_argument("--extra-slots", type=int, default=64,
                     help="v3_decode_serving: copies of hot experts beyond one slot per expert")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--wgrad-dtype", default="bf16", choices=["bf16", "f32"],
+                    help="v3_prefill_backward: dtype of the weight gradients")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens of the batch the CPU oracle runs (default: 64 for v3_skew, whose tokens "
@@ -198,6 +202,7 @@ def build_layer(cfg, d, torch, dsi):
     del w13_all, w2_all
     torch.cuda.empty_cache()
     weights = d.MoEWeights(q13[:E], s13[:E], q2[:E], s2[:E], q13[E], s13[E], q2[E], s2[E], wr)
+    weights.stacked = (q13, s13, q2, s2)      # routed experts, then the shared one
     return x, bias, weights, statistics.median(times)
 
 
@@ -647,27 +652,22 @@ def run_serving(args, torch):
     print(json.dumps(result), flush=True)
 
 
-def run_dgrad(args, torch):
+def run_backward(args, torch):
     import fp8_block_scaled_dsmoe_amd as d
     import dsmoe_inputs as dsi
     cfg = dsi.LAYER_CONFIGS["v3_prefill"]
     T, H, I, E, K = cfg.T, cfg.H, cfg.I, cfg.E, cfg.K
-    TK = T * K
-    log(f"workload v3_prefill_dgrad: T={T} H={H} E={E} K={K} I={I}, routed experts")
+    rows = T * K + T
+    wdt = torch.bfloat16 if args.wgrad_dtype == "bf16" else torch.float32
+    log(f"workload v3_prefill_backward: T={T} H={H} E={E} K={K} I={I}, routed experts + shared, "
+        f"weight gradients {args.wgrad_dtype}")
     x, bias, weights, _ = build_layer(cfg, d, torch, dsi)
     desc = d.MoEDesc(H, I, E, cfg.G, cfg.Mg, K, 1)
     _, counts, dbg = d.moe_forward(desc, weights, bias, x, debug=True)
-    perm, offsets = dbg["perm"], dbg["offsets"]
+    w = weights.stacked
     g = torch.Generator(device="cuda")
     g.manual_seed(5)
     dy = torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16)
-    dh = torch.randn((TK, 2 * I), device="cuda", generator=g).to(torch.bfloat16)
-    qdy, sdy = d.quant_act_1x128(dy)
-    qdh, sdh = d.quant_act_1x128(dh)
-    w2t, s2t = d.transpose_w_128x128(weights.w2, weights.s2)
-    w13t, s13t = d.transpose_w_128x128(weights.w13, weights.s13)
-    da = torch.empty((TK, I), dtype=torch.float32, device="cuda")
-    dxr = torch.empty((TK, H), dtype=torch.bfloat16, device="cuda")
 
     def timed(fn):
         for _ in range(args.warmup):
@@ -683,27 +683,40 @@ def run_dgrad(args, torch):
             ts.append(e0.elapsed_time(e1))
         return statistics.median(ts)
 
-    t_w2 = timed(lambda: d.transpose_w_128x128(weights.w2, weights.s2))
-    t_w13 = timed(lambda: d.transpose_w_128x128(weights.w13, weights.s13))
-    t_down = timed(lambda: d.fp8_grouped_gemm(qdy, sdy, offsets, w2t, s2t, a_rows=perm, m_total=TK, c=da))
-    t_up = timed(lambda: d.fp8_grouped_gemm(qdh, sdh, offsets, w13t, s13t, c=dxr))
-    touched = int((counts > 0).sum().item())
-    fl_down = 2.0 * TK * H * I
-    fl_up = 2.0 * TK * 2 * I * H
-    b_down = touched * H * I + TK * I * 4 + T * H       # W2^T streamed, f32 out, dy codes
-    b_up = touched * 2 * I * H + TK * H * 2 + TK * 2 * I  # W13^T streamed, bf16 out, dh codes
-    gb = lambda b, ms: b / (ms * 1e-3) / 1e9
-    tf = lambda f, ms: f / (ms * 1e-3) / 1e12
-    tr_bytes_w2, tr_bytes_w13 = 2 * E * H * I, 2 * E * 2 * I * H
-    log(f"transpose W2 {t_w2:.3f} ms ({gb(tr_bytes_w2, t_w2):.0f} GB/s), W13 {t_w13:.3f} ms "
-        f"({gb(tr_bytes_w13, t_w13):.0f} GB/s)")
-    log(f"dgrad down (dy.W2) {t_down:.3f} ms: {tf(fl_down, t_down):.0f} TFLOP/s, {gb(b_down, t_down):.0f} GB/s; "
-        f"dgrad up (dh.W13) {t_up:.3f} ms: {tf(fl_up, t_up):.0f} TFLOP/s, {gb(b_up, t_up):.0f} GB/s")
-    ms = t_down + t_up
+    # the weights' block transposes: once per weight version, outside the step
+    t_tr = timed(lambda: (d.transpose_w_128x128(w[0], w[1]), d.transpose_w_128x128(w[2], w[3])))
+    wt = d.transpose_w_128x128(w[0], w[1]) + d.transpose_w_128x128(w[2], w[3])
+    for _ in range(args.warmup):
+        d.moe_backward_experts(dbg, x, dy, w, wt, T, K, wgrad_dtype=wdt)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        out = d.moe_backward_experts(dbg, x, dy, w, wt, T, K, wgrad_dtype=wdt, stage_events=ev[i])
+        del out
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    stage = {n: statistics.mean(r[j].elapsed_time(r[j + 1]) for r in ev) for j, n in enumerate(d.BACKWARD_STAGES)}
+    touched = int((counts > 0).sum().item()) + 1
+    gb = lambda b, t: b / (t * 1e-3) / 1e9
+    tf = lambda f, t: f / (t * 1e-3) / 1e12
+    # FP8 GEMM flops of the step: recomputed h (2I x H) and o (H x I), the two
+    # dgrads and the two weight gradients
+    gemm_flops = 2.0 * rows * H * I * (2 + 1 + 1 + 2 + 1 + 2)
+    esz = 2 if wdt == torch.bfloat16 else 4
+    w13_out = (E + 1) * 2 * I * H * esz
+    # the weight gradient of W13: every expert's [2I][H] written once, plus the
+    # token-tile codes and scales of dh and x it reads (x read once per expert)
+    wg13_bytes = w13_out + rows * (2 * I + H) + rows // 128 * (2 * I + H) * 4
+    wg13_ms = stage["wgrad_w13"]
+    log(f"{args.steps} steps: {ms:.3f} ms/step; stages " + ", ".join(f"{k} {v:.3f}" for k, v in stage.items()) +
+        f"; transposes {t_tr:.3f} ms per weight version")
     result = {
         "metric": METRIC,
-        "value": round(tf(fl_down + fl_up, ms), 2),
-        "unit": "TFLOP/s",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -712,18 +725,20 @@ def run_dgrad(args, torch):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3",
-        "data": "synthetic",
-        "config": {"workload": f"v3_prefill_dgrad: FP8 data-gradient grouped GEMMs of the routed experts, "
-                               f"dy.W2 and dh.W13 on block-transposed weights, T={T}, H={H}, E={E}, "
-                               f"top-{K}, I={I}", "T": T, "H": H, "E": E, "K": K, "I": I},
-        "roofline": {"bound": "hbm", "achieved": round(gb(b_up, t_up), 2), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(gb(b_up, t_up) / PEAK_HBM_GBPS, 4), "traffic": None,
-                     "kernel": "dgrad of the gate/up projection, dh . W13 (grouped FP8 GEMM)",
-                     "algorithmic_bytes": int(b_up), "algorithmic_flops": fl_up, "avg_ms": round(t_up, 4)},
-        "dgrad_down": {"ms": round(t_down, 4), "tflops": round(tf(fl_down, t_down), 2),
-                       "gbps": round(gb(b_down, t_down), 1), "algorithmic_bytes": int(b_down)},
-        "transpose_ms": {"w2": round(t_w2, 4), "w13": round(t_w13, 4),
-                         "gbps": round(gb(tr_bytes_w2 + tr_bytes_w13, t_w2 + t_w13), 1)},
+        "data": "synthetic (dy ~ N(0,1) stands in for the loss gradient; every other input is the forward's)",
+        "config": {"workload": f"v3_prefill_backward: FP8 backward of the routed and shared experts on the "
+                               f"forward's intermediates (recomputed h and o, gate and router-logit gradients, "
+                               f"both dgrads, SwiGLU backward, both weight gradients in {args.wgrad_dtype}), "
+                               f"T={T}, H={H}, E={E}, top-{K}, I={I}",
+                   "T": T, "H": H, "E": E, "K": K, "I": I},
+        "roofline": {"bound": "hbm", "achieved": round(gb(wg13_bytes, wg13_ms), 2), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(gb(wg13_bytes, wg13_ms) / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "weight gradient of W13 (grouped FP8 Wgrad GEMM over each expert's tokens)",
+                     "algorithmic_bytes": int(wg13_bytes), "avg_ms": round(wg13_ms, 4)},
+        "grouped_gemm_tflops": round(tf(gemm_flops, ms), 2),
+        "grouped_gemm_frac_mfma_peak": round(tf(gemm_flops, ms) / PEAK_FP8_TFLOPS, 4),
+        "stage_ms": {k: round(v, 4) for k, v in stage.items()},
+        "transpose_ms_per_weight_version": round(t_tr, 4),
         "experts_touched": touched,
     }
     print(json.dumps(result), flush=True)
@@ -748,8 +763,8 @@ def main():
     if args.workload == "v3_decode_serving":
         run_serving(args, torch)
         return
-    if args.workload == "v3_prefill_dgrad":
-        run_dgrad(args, torch)
+    if args.workload == "v3_prefill_backward":
+        run_backward(args, torch)
         return
     import fp8_block_scaled_dsmoe_amd as d
     import dsmoe_inputs as dsi

@@ -84,6 +84,18 @@ lib.dsmoe_moe_forward_noalloc.restype = _int
 lib.dsmoe_moe_forward_noalloc.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Weights), _vp, _vp, _i64, _vp,
                                           _int, _vp, ctypes.POINTER(_Debug), _vp]
 NOALLOC_SCRATCH_BYTES = 80 << 20
+lib.dsmoe_token_tiles.restype = _i64
+lib.dsmoe_token_tiles.argtypes = [_i64, _i32]
+lib.dsmoe_quant_tokens_128.restype = _int
+lib.dsmoe_quant_tokens_128.argtypes = [_vp, _int, _i64, _i64, _vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp]
+lib.dsmoe_fp8_wgrad_grouped.restype = _int
+lib.dsmoe_fp8_wgrad_grouped.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _int, _vp]
+lib.dsmoe_swiglu_backward.restype = _int
+lib.dsmoe_swiglu_backward.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp]
+lib.dsmoe_gate_backward.restype = _int
+lib.dsmoe_gate_backward.argtypes = [_vp, _vp, _int, _vp, _vp, _vp, _i64, _i32, _i32, _i64, _vp, _vp, _vp]
+lib.dsmoe_combine_rows.restype = _int
+lib.dsmoe_combine_rows.argtypes = [_vp, _int, _vp, _i64, _i32, _i64, _i64, _vp, _vp]
 lib.dsmoe_update_bias.restype = _int
 lib.dsmoe_update_bias.argtypes = [_vp, _vp, _i32, _i64, _i32, ctypes.c_float, _vp]
 lib.dsmoe_quant_rows.restype = _int
@@ -115,7 +127,9 @@ EXPORTED = ("dsmoe_status_str", "dsmoe_abi_version", "dsmoe_quant_act_1x128", "d
             "dsmoe_update_bias", "dsmoe_quant_rows", "dsmoe_quant_tensor",
             "dsmoe_gemm_granularity_workspace_bytes", "dsmoe_fp8_gemm_granularity",
             "dsmoe_plan_replicas", "dsmoe_place_replicas", "dsmoe_slot_offsets", "dsmoe_moe_serving_workspace_bytes",
-            "dsmoe_moe_forward_serving", "dsmoe_transpose_w_128x128", "dsmoe_moe_forward_noalloc")
+            "dsmoe_moe_forward_serving", "dsmoe_transpose_w_128x128", "dsmoe_moe_forward_noalloc",
+            "dsmoe_token_tiles", "dsmoe_quant_tokens_128", "dsmoe_fp8_wgrad_grouped", "dsmoe_swiglu_backward",
+            "dsmoe_gate_backward", "dsmoe_combine_rows")
 
 # dsmoe_granularity codes
 GRANULARITIES = {"tensor": 0, "channel": 1, "block": 2}
@@ -482,6 +496,186 @@ def moe_forward_noalloc(desc: MoEDesc, weights: MoEWeights, bias: torch.Tensor, 
                                          ctypes.byref(dbg_c) if dbg_c is not None else None, _stream()),
            "dsmoe_moe_forward_noalloc")
     return y, counts, dbg
+
+
+def token_tiles(m_total: int, n_groups: int) -> int:
+    """Upper bound on the 128-row token tiles of m_total rows in n_groups groups."""
+    return int(lib.dsmoe_token_tiles(m_total, n_groups))
+
+
+def quant_tokens_128(src: torch.Tensor, offsets: torch.Tensor, m_total: Optional[int] = None,
+                     rows: Optional[torch.Tensor] = None, row_scale: Optional[torch.Tensor] = None):
+    """1x128 tiles along the rows of each group (dsmoe_quant_tokens_128).
+
+    src bf16/f32 [n_src][C]; offsets int32 [G+1] (device); rows int32
+    [m_total] (source row per output row) or None; row_scale f32 [m_total]
+    or None.  Returns (qt uint8 [C][P], scales f32 [P/128][C], chunk_off
+    int32 [G+1])."""
+    if src.dtype not in (torch.bfloat16, torch.float32) or not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous bf16 or f32 CUDA tensor")
+    _dev(offsets, torch.int32, "offsets")
+    if rows is not None:
+        _dev(rows, torch.int32, "rows")
+    if row_scale is not None:
+        _dev(row_scale, torch.float32, "row_scale")
+    G = offsets.numel() - 1
+    n_src, C = src.shape
+    if m_total is None:
+        m_total = rows.numel() if rows is not None else n_src
+    P = 128 * token_tiles(m_total, G)
+    dev = src.device
+    qt = torch.empty((C, max(P, 128)), dtype=torch.uint8, device=dev)
+    sc = torch.empty((max(P, 128) // 128, C), dtype=torch.float32, device=dev)
+    cho = torch.empty((G + 1,), dtype=torch.int32, device=dev)
+    _check(lib.dsmoe_quant_tokens_128(_p(src), _dtype_code(src.dtype), n_src, C, _p(rows), _p(row_scale),
+                                      _p(offsets), G, m_total, _p(cho), _p(qt), _p(sc), _stream()),
+           "dsmoe_quant_tokens_128")
+    return qt[:, :P], sc[:P // 128], cho
+
+
+def fp8_wgrad_grouped(at: torch.Tensor, sa: torch.Tensor, bt: torch.Tensor, sb: torch.Tensor,
+                      chunk_off: torch.Tensor, out_dtype=torch.float32, c: Optional[torch.Tensor] = None):
+    """Per-group weight gradient c[g] = A_g B_g^T over the group's token tiles
+    (dsmoe_fp8_wgrad_grouped); at/sa and bt/sb from quant_tokens_128 on the
+    same offsets.  Returns c [G][M][N]."""
+    _dev(at, torch.uint8, "at")
+    _dev(bt, torch.uint8, "bt")
+    _dev(sa, torch.float32, "sa")
+    _dev(sb, torch.float32, "sb")
+    _dev(chunk_off, torch.int32, "chunk_off")
+    G = chunk_off.numel() - 1
+    M, P = at.shape
+    N = bt.shape[0]
+    if bt.shape[1] != P:
+        raise ValueError("at and bt must span the same token tiles")
+    if c is None:
+        c = torch.empty((G, M, N), dtype=out_dtype, device=at.device)
+    # the codes' rows are P apart: pass the strided views' base with P as the stride
+    _check(lib.dsmoe_fp8_wgrad_grouped(_p(at), _p(sa), _p(bt), _p(sb), _p(chunk_off), G, M, N,
+                                       at.stride(0), _p(c), _dtype_code(c.dtype), _stream()),
+           "dsmoe_fp8_wgrad_grouped")
+    return c
+
+
+def swiglu_backward(h: torch.Tensor, da: torch.Tensor, row_gate: Optional[torch.Tensor] = None,
+                    recompute_a: bool = False):
+    """SwiGLU backward on the recomputed activation (dsmoe_swiglu_backward).
+    h f32 [rows][2I], da f32 [rows][I], row_gate f32 [rows] or None.
+    Returns (dh f32 [rows][2I], a f32 [rows][I] or None)."""
+    _dev(h, torch.float32, "h")
+    _dev(da, torch.float32, "da")
+    if row_gate is not None:
+        _dev(row_gate, torch.float32, "row_gate")
+    rows, I = da.shape
+    dh = torch.empty((rows, 2 * I), dtype=torch.float32, device=h.device)
+    a = torch.empty((rows, I), dtype=torch.float32, device=h.device) if recompute_a else None
+    _check(lib.dsmoe_swiglu_backward(_p(h), _p(da), _p(row_gate), rows, I, _p(dh), _p(a), _stream()),
+           "dsmoe_swiglu_backward")
+    return dh, a
+
+
+def gate_backward(dy: torch.Tensor, o: torch.Tensor, inv: torch.Tensor, topk_idx: torch.Tensor,
+                  logits: torch.Tensor):
+    """Gradients of the gates and the router logits (dsmoe_gate_backward).
+    dy bf16 [T][H]; o bf16/f32 [T*K][H] ungated expert outputs; inv, topk_idx
+    int32 [T][K]; logits f32 [T][E].  Returns (dgate f32 [T][K], dlogits f32
+    [T][E])."""
+    _dev(dy, torch.bfloat16, "dy")
+    _dev(inv, torch.int32, "inv")
+    _dev(topk_idx, torch.int32, "topk_idx")
+    _dev(logits, torch.float32, "logits")
+    T, H = dy.shape
+    K = topk_idx.shape[1]
+    E = logits.shape[1]
+    dgate = torch.empty((T, K), dtype=torch.float32, device=dy.device)
+    dlogits = torch.empty((T, E), dtype=torch.float32, device=dy.device)
+    _check(lib.dsmoe_gate_backward(_p(dy), _p(o), _dtype_code(o.dtype), _p(inv), _p(topk_idx), _p(logits), T, E,
+                                   K, H, _p(dgate), _p(dlogits), _stream()), "dsmoe_gate_backward")
+    return dgate, dlogits
+
+
+def combine_rows(o: torch.Tensor, inv: torch.Tensor, shared0: int = -1, y: Optional[torch.Tensor] = None):
+    """y[t] = o[shared0 + t] (if shared0 >= 0) + sum_k o[inv[t][k]] in float32
+    (dsmoe_combine_rows); o and y bf16 or f32."""
+    _dev(inv, torch.int32, "inv")
+    T, K = inv.shape
+    H = o.shape[1]
+    if y is None:
+        y = torch.empty((T, H), dtype=o.dtype, device=o.device)
+    _check(lib.dsmoe_combine_rows(_p(o), _dtype_code(o.dtype), _p(inv), T, K, H, shared0, _p(y), _stream()),
+           "dsmoe_combine_rows")
+    return y
+
+
+def expert_rows(dbg: dict, T: int, K: int, n_shared: int = 1):
+    """The forward's row structure over the routed groups and the shared one
+    (index plumbing only): offsets [E+1+n_shared], perm [T*K + n_shared*T]
+    (row -> token) and the row gates (gate of each routed row, 1 for the
+    shared expert's rows), from a debug dict of moe_forward."""
+    dev = dbg["perm"].device
+    rows = T * K + (T if n_shared else 0)
+    off, perm = dbg["offsets"], dbg["perm"]
+    rg = torch.ones((rows,), dtype=torch.float32, device=dev)
+    rg[dbg["inv"].reshape(-1).long()] = dbg["gates"].reshape(-1)
+    if n_shared:
+        off = torch.cat([off, torch.tensor([rows], dtype=torch.int32, device=dev)])
+        perm = torch.cat([perm, torch.arange(T, dtype=torch.int32, device=dev)])
+    return off, perm, rg
+
+
+def moe_backward_experts(dbg: dict, x: torch.Tensor, dy: torch.Tensor, w, wt, T: int, K: int,
+                         n_shared: int = 1, wgrad_dtype=torch.float32, stage_events=None):
+    """The FP8 backward of the routed experts and the shared one, as a chain of
+    the library's calls on the forward's intermediates (dbg from moe_forward
+    with debug=True: routing, x codes, codes of a).
+
+    x bf16 [T][H] (the layer input), dy bf16 [T][H] (gradient of y);
+    w = (q13, s13, q2, s2) and wt = their block transposes, over the routed
+    experts followed by the shared one.  Steps: h = x W13^T recomputed (the
+    SwiGLU input) and the ungated expert outputs o = a W2^T; the gate and
+    router-logit gradients; the dgrad of the down projection; the SwiGLU
+    backward (recomputing a); the dgrad of the gate/up projection, summed per
+    token; the weight gradients dW2 and dW13 on 1x128 tiles along each
+    expert's tokens.  stage_events: optional 9 torch.cuda.Events recorded at
+    the start and after each of the 8 steps.  Returns a dict of device
+    tensors: h, o, dgate, dlogits, da, dh, a, dx, dw2, dw13."""
+    off, perm, rg = expert_rows(dbg, T, K, n_shared)
+    rows = perm.numel()
+    q13, s13, q2, s2 = w
+    q13t, s13t, q2t, s2t = wt
+    ev = stage_events or [None] * 9
+    mark = lambda i: ev[i].record() if ev[i] is not None else None
+    out = {}
+    mark(0)
+    out["h"] = fp8_grouped_gemm(dbg["qx"], dbg["sx"], off, q13, s13, out_dtype=torch.float32, a_rows=perm,
+                                m_total=rows)
+    out["o"] = fp8_grouped_gemm(dbg["qa"], dbg["sa"], off, q2, s2, out_dtype=torch.float32, m_total=rows)
+    mark(1)
+    out["dgate"], out["dlogits"] = gate_backward(dy, out["o"], dbg["inv"], dbg["topk_idx"], dbg["logits"])
+    mark(2)
+    qdy, sdy = quant_act_1x128(dy)
+    out["da"] = fp8_grouped_gemm(qdy, sdy, off, q2t, s2t, out_dtype=torch.float32, a_rows=perm, m_total=rows)
+    mark(3)
+    out["dh"], out["a"] = swiglu_backward(out["h"], out["da"], rg, recompute_a=True)
+    mark(4)
+    qdh, sdh = quant_act_1x128(out["dh"])
+    dx_rows = fp8_grouped_gemm(qdh, sdh, off, q13t, s13t, out_dtype=torch.float32, m_total=rows)
+    out["dx"] = combine_rows(dx_rows, dbg["inv"], shared0=T * K if n_shared else -1)
+    mark(5)
+    qdo, sdo, cho = quant_tokens_128(dy, off, m_total=rows, rows=perm, row_scale=rg)
+    qa_t, sa_t, _ = quant_tokens_128(out["a"], off)
+    qdh_t, sdh_t, _ = quant_tokens_128(out["dh"], off)
+    qx_t, sx_t, _ = quant_tokens_128(x, off, m_total=rows, rows=perm)
+    mark(6)
+    out["dw2"] = fp8_wgrad_grouped(qdo, sdo, qa_t, sa_t, cho, out_dtype=wgrad_dtype)
+    mark(7)
+    out["dw13"] = fp8_wgrad_grouped(qdh_t, sdh_t, qx_t, sx_t, cho, out_dtype=wgrad_dtype)
+    mark(8)
+    return out
+
+
+BACKWARD_STAGES = ("recompute_h_and_o", "gate_router_grad", "dgrad_down", "swiglu_backward",
+                   "dgrad_gate_up_and_sum", "token_tiles", "wgrad_w2", "wgrad_w13")
 
 
 def plan_replicas(counts: torch.Tensor, n_extra: int):

@@ -812,4 +812,93 @@ dsmoe_status dsmoe_moe_forward_serving(const dsmoe_moe_desc* d, const dsmoe_moe_
   return DSMOE_OK;
 }
 
+int64_t dsmoe_token_tiles(int64_t M_total, int32_t G) {
+  if (M_total < 0 || G < 1) return 0;
+  return dsmoe::token_tiles(M_total, G);
+}
+
+dsmoe_status dsmoe_quant_tokens_128(const void* src, int src_type, int64_t n_src, int64_t C,
+                                    const int32_t* rows, const float* row_scale, const int32_t* offsets,
+                                    int32_t G, int64_t M_total, int32_t* chunk_off, uint8_t* qt,
+                                    float* scales, void* stream) {
+  if (!valid_dtype(src_type)) return DSMOE_ERR_DTYPE;
+  if (G < 1 || G > 65536 || M_total < 0 || n_src < 0 || C <= 0 || C % 128) return DSMOE_ERR_SHAPE;
+  if (!rows && n_src < M_total) return DSMOE_ERR_SHAPE;
+  const int64_t tiles = dsmoe::token_tiles(M_total, G);
+  if (tiles > kI32Max || C / 128 > 65535 || C * tiles * 128 > (1LL << 40)) return DSMOE_ERR_SHAPE;
+  if (!offsets || !chunk_off) return DSMOE_ERR_NULL;
+  if (M_total > 0 && (!src || !qt || !scales)) return DSMOE_ERR_NULL;
+  if ((src && !aligned(src, 16)) || (qt && !aligned(qt, 16)) || (scales && !aligned(scales, 4)) ||
+      !aligned(offsets, 4) || !aligned(chunk_off, 4) || (rows && !aligned(rows, 4)) ||
+      (row_scale && !aligned(row_scale, 4)))
+    return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  return launch_status(dsmoe::launch_quant_tokens(src, src_type == DSMOE_F32, C, rows, row_scale, offsets, G,
+                                                  M_total, chunk_off, qt, scales,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+dsmoe_status dsmoe_fp8_wgrad_grouped(const uint8_t* at, const float* sa, const uint8_t* bt, const float* sb,
+                                     const int32_t* chunk_off, int32_t G, int64_t M, int64_t N, int64_t P,
+                                     void* c, int ct, void* stream) {
+  if (!valid_dtype(ct)) return DSMOE_ERR_DTYPE;
+  if (G < 1 || M <= 0 || N <= 0 || M % 128 || N % 128 || P < 0 || P % 128) return DSMOE_ERR_SHAPE;
+  if (static_cast<int64_t>(G) * (M / 128) * (N / 128) > kI32Max) return DSMOE_ERR_SHAPE;
+  if (!at || !sa || !bt || !sb || !chunk_off || !c) return DSMOE_ERR_NULL;
+  if (!aligned(at, 16) || !aligned(bt, 16) || !aligned(c, 16) || !aligned(sa, 16) || !aligned(sb, 16) ||
+      !aligned(chunk_off, 4))
+    return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  return launch_status(dsmoe::launch_wgrad(at, sa, bt, sb, chunk_off, G, M, N, P, c, ct == DSMOE_F32,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+dsmoe_status dsmoe_swiglu_backward(const float* h, const float* da, const float* row_gate, int64_t rows,
+                                   int64_t I, float* dh, float* a_out, void* stream) {
+  if (rows < 0 || I <= 0 || I % 128 || rows > kI32Max) return DSMOE_ERR_SHAPE;
+  if (rows == 0) return DSMOE_OK;
+  if (!h || !da || !dh) return DSMOE_ERR_NULL;
+  if (!aligned(h, 16) || !aligned(da, 16) || !aligned(dh, 16) || (a_out && !aligned(a_out, 16)) ||
+      (row_gate && !aligned(row_gate, 4)))
+    return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  return launch_status(dsmoe::launch_swiglu_bwd(h, da, row_gate, rows, I, dh, a_out,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+dsmoe_status dsmoe_gate_backward(const void* dy, const void* o, int ot, const int32_t* inv,
+                                 const int32_t* topk_idx, const float* logits, int64_t T, int32_t E,
+                                 int32_t K, int64_t H, float* dgate, float* dlogits, void* stream) {
+  if (!valid_dtype(ot)) return DSMOE_ERR_DTYPE;
+  if (T < 0 || T > kI32Max || K < 1 || K > DSMOE_MAX_TOPK || E < K || E > DSMOE_MAX_EXPERTS || H <= 0 ||
+      H % 8)
+    return DSMOE_ERR_SHAPE;
+  if (T == 0) return DSMOE_OK;
+  if (!dy || !o || !inv || !topk_idx || !logits || !dgate || !dlogits) return DSMOE_ERR_NULL;
+  if (!aligned(dy, 16) || !aligned(o, 16) || !aligned(inv, 4) || !aligned(topk_idx, 4) || !aligned(logits, 4) ||
+      !aligned(dgate, 4) || !aligned(dlogits, 4))
+    return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  return launch_status(dsmoe::launch_gate_grad(static_cast<const uint16_t*>(dy), o, ot == DSMOE_F32, inv,
+                                               topk_idx, logits, T, E, K, H, dgate, dlogits,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+dsmoe_status dsmoe_combine_rows(const void* o, int ot, const int32_t* inv, int64_t T, int32_t K, int64_t H,
+                                int64_t shared0, void* y, void* stream) {
+  if (!valid_dtype(ot)) return DSMOE_ERR_DTYPE;
+  if (T < 0 || K < 1 || H <= 0 || H % 8 || T * (K + 1) > kI32Max) return DSMOE_ERR_SHAPE;
+  if (T == 0) return DSMOE_OK;
+  if (!o || !inv || !y) return DSMOE_ERR_NULL;
+  if (!aligned(o, 16) || !aligned(y, 16) || !aligned(inv, 4)) return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  return launch_status(dsmoe::launch_combine(o, inv, T, K, H, shared0, y, ot == DSMOE_F32,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -70,4 +70,21 @@ hipError_t launch_permute(const int32_t* topk_idx, const float* gates, int64_t T
 hipError_t launch_update_bias(float* bias, const int32_t* counts, int32_t E, int64_t T,
                               int32_t K, float gamma, hipStream_t s);
 
+// backward.hip
+// upper bound on the 128-row token tiles of m_total rows in G groups
+int64_t token_tiles(int64_t m_total, int32_t G);
+// chunk offsets cho [G+1] of the groups, then codes qt [C][P] and scales st
+// [P/128][C] of the 1x128 tiles along each group's rows, P = 128 * token_tiles
+hipError_t launch_quant_tokens(const void* src, bool f32, int64_t C, const int32_t* rows, const float* row_scale,
+                               const int32_t* offsets, int32_t G, int64_t m_total, int32_t* cho, uint8_t* qt,
+                               float* st, hipStream_t s);
+// c[g] [M][N] (f32 or bf16) = A_g B_g^T over group g's token tiles
+hipError_t launch_wgrad(const uint8_t* at, const float* sat, const uint8_t* bt, const float* sbt, const int32_t* cho,
+                        int32_t G, int64_t M, int64_t N, int64_t P, void* c, bool f32, hipStream_t s);
+hipError_t launch_swiglu_bwd(const float* h, const float* da_raw, const float* row_gate, int64_t rows, int64_t I,
+                             float* dh, float* a_out, hipStream_t s);
+hipError_t launch_gate_grad(const uint16_t* dy, const void* o, bool o_f32, const int32_t* inv, const int32_t* topk,
+                            const float* logits, int64_t T, int32_t E, int32_t K, int64_t H, float* dgate,
+                            float* dlogits, hipStream_t s);
+
 }  // namespace dsmoe

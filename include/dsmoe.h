@@ -426,6 +426,109 @@ dsmoe_status dsmoe_moe_forward_serving(const dsmoe_moe_desc* d, const dsmoe_moe_
                                        size_t ws_bytes, const dsmoe_moe_debug* dbg, void* stream);
 
 /*
+ * The rest of the FP8 backward of the expert FFN.  Source: V3 notes §6 (the
+ * Fprop, Dgrad and Wgrad GEMMs of every Linear in FP8 E4M3, outputs BF16 or
+ * FP32; 1x128 tiles for activations, 128x128 blocks for weights; partial
+ * sums promoted to FP32 every 128 products, §6.1, §6.2); infra answer,
+ * memory paragraph (SwiGLU is recomputed in the backward); V3 notes §4
+ * (gates from the raw affinity, the bias only selects).  The pages do not
+ * orient the gradient tiles: here every FP8 operand is tiled 1x128 along its
+ * GEMM's contraction axis, so the weight-gradient GEMMs, which contract over
+ * an expert's tokens, take both operands in tiles of 128 consecutive rows of
+ * the expert's group.
+ */
+
+/* Upper bound on the 128-row token tiles of M_total rows in G groups
+ * (sum over groups of ceil(n_g / 128)); sizes the buffers below. */
+int64_t dsmoe_token_tiles(int64_t M_total, int32_t G);
+
+/*
+ * dsmoe_quant_tokens_128 -- 1x128 tiles along the rows of each group.
+ *   src        [n_src][C] bf16 or f32 (src_type), row-major, C % 128 == 0
+ *   rows       [M_total] int32 source row of each output row (NULL: row r
+ *              is src row r), each in [0, n_src)
+ *   row_scale  [M_total] f32 or NULL: row r is fl32(row_scale[r] * src)
+ *              (e.g. the gate of the down projection's output gradient)
+ *   offsets    [G+1] int32 on the device: group g holds rows offsets[g] ..
+ *              offsets[g+1]-1 (nondecreasing, offsets[G] <= M_total)
+ *   chunk_off  [G+1] int32 (output): first tile of each group, the
+ *              exclusive scan of ceil(n_g / 128)
+ *   qt         [C][P] codes (output), P = 128 * dsmoe_token_tiles(M_total, G):
+ *              tile j of group g, column c is qt[c][128 (chunk_off[g] + j) ..
+ *              + 127], row by row; rows past the group's end are code 0
+ *   scales     [P/128][C] f32 (output): scales[chunk_off[g] + j][c]
+ * Per tile and column: amax over its rows, scale = fl32(amax / 448) (1 for
+ * an all-zero column), codes E4M3 of the IEEE quotients, round to nearest
+ * even, saturating.  Columns of qt past the used tiles are not written.
+ * Requires 1 <= G <= 65536, M_total >= 0, C > 0.
+ */
+dsmoe_status dsmoe_quant_tokens_128(const void* src, int src_type, int64_t n_src, int64_t C,
+                                    const int32_t* rows, const float* row_scale, const int32_t* offsets,
+                                    int32_t G, int64_t M_total, int32_t* chunk_off, uint8_t* qt,
+                                    float* scales, void* stream);
+
+/*
+ * dsmoe_fp8_wgrad_grouped -- weight-gradient GEMM of every group.
+ *   at, sa     [M][P] codes and [P/128][M] scales of the output gradient,
+ *              transposed (dsmoe_quant_tokens_128 over its M columns)
+ *   bt, sb     [N][P] codes and [P/128][N] scales of the GEMM input, likewise
+ *   chunk_off  [G+1] the groups' tiles (from dsmoe_quant_tokens_128)
+ *   c          [G][M][N] output (ct: DSMOE_BF16 or DSMOE_F32):
+ *              c[g][m][n] = sum over tiles t of group g of
+ *              sa[t][m] * sb[t][n] * sum_k dec(at[m][128t+k]) dec(bt[n][128t+k]),
+ *              each tile's partial sum promoted to FP32; 0 for a group
+ *              without rows
+ * For the down projection o = a W2^T: at = quantised do^T (M = H), bt =
+ * quantised a^T (N = I), c = dW2 [G][H][I].  For the gate/up projection:
+ * at = quantised dh^T (M = 2I), bt = quantised x^T (N = H), c = dW13.
+ * Requires M, N positive multiples of 128, 1 <= G, P a multiple of 128.
+ */
+dsmoe_status dsmoe_fp8_wgrad_grouped(const uint8_t* at, const float* sa, const uint8_t* bt, const float* sb,
+                                     const int32_t* chunk_off, int32_t G, int64_t M, int64_t N, int64_t P,
+                                     void* c, int ct, void* stream);
+
+/*
+ * dsmoe_swiglu_backward -- SwiGLU backward on the recomputed activation.
+ *   h         [rows][2I] f32: the gate/up GEMM output (gate columns, then up)
+ *   da        [rows][I] f32: gradient of the expert's SwiGLU output before
+ *             the gate factor (the down projection's dgrad output)
+ *   row_gate  [rows] f32 or NULL (1): the row's gate, multiplied in first
+ *   dh        [rows][2I] f32 (output): with d = row_gate * da, sig = 1 /
+ *             (1 + e^-g): dh_gate = d u sig (1 + g (1 - sig)), dh_up = d g sig
+ *   a_out     [rows][I] f32 or NULL: the recomputed a = g sig u
+ * Requires I % 128 == 0, rows >= 0.
+ */
+dsmoe_status dsmoe_swiglu_backward(const float* h, const float* da, const float* row_gate, int64_t rows,
+                                   int64_t I, float* dh, float* a_out, void* stream);
+
+/*
+ * dsmoe_gate_backward -- gradients of the gates and of the router logits.
+ *   dy        [T][H] bf16: gradient of the layer output y
+ *   o         [T*K][H] (ot: bf16 or f32): the routed experts' ungated
+ *             outputs, row inv[t][k] for token t's k-th expert
+ *   inv       [T][K], topk_idx [T][K] int32, logits [T][E] f32: the forward's
+ *   dgate     [T][K] f32 (output): dgate[t][k] = <dy[t], o[inv[t][k]]>
+ *   dlogits   [T][E] f32 (output): with s = fl32(sigmoid(z)) (double
+ *             evaluation, as the routing), S = sum of the chosen s, gate =
+ *             s / S: s_k (1 - s_k) (dgate_k - sum_j dgate_j gate_j) / S at
+ *             the chosen experts, 0 elsewhere (routing held fixed)
+ * Requires H % 8 == 0, 1 <= K <= DSMOE_MAX_TOPK, K <= E <= DSMOE_MAX_EXPERTS.
+ */
+dsmoe_status dsmoe_gate_backward(const void* dy, const void* o, int ot, const int32_t* inv,
+                                 const int32_t* topk_idx, const float* logits, int64_t T, int32_t E,
+                                 int32_t K, int64_t H, float* dgate, float* dlogits, void* stream);
+
+/*
+ * dsmoe_combine_rows -- the forward's combine over rows of (token, expert)
+ * results: y[t] = o[shared0 + t] (when shared0 >= 0) + sum over k ascending of
+ * o[inv[t][k]], summed in float32 (e.g. the input gradient of the gate/up
+ * projection from its per-row dgrad).  o and y share the type ot (bf16 or
+ * f32), rows of H columns.  Requires H % 8 == 0.
+ */
+dsmoe_status dsmoe_combine_rows(const void* o, int ot, const int32_t* inv, int64_t T, int32_t K, int64_t H,
+                                int64_t shared0, void* y, void* stream);
+
+/*
  * Coarser scaling granularities, for comparison with the recipe's 1x128 /
  * 128x128 tiles.  Source: infra answer, FP8 paragraph (per-tensor E4M3
  * scaling lets a single outlier stretch the scale of a whole tensor and so
