@@ -331,6 +331,7 @@ dsmoe_status dsmoe_fp8_grouped_gemm(const uint8_t* a, const float* a_scale,
   p.epi = dsmoe::Epilogue::kStore;
   p.row_limit = M_total;
   p.rows_hint = (M_total + G - 1) / G;
+  p.a_rows_total = a_rows ? 0 : M_total;   // with a gather A's row count is not known
   return launch_status(dsmoe::launch_grouped_gemm(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -438,6 +439,7 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
   g1.epi = dsmoe::Epilogue::kSwiGLUQuant;
   g1.row_limit = g1.M_total;
   g1.rows_hint = (T * K + E - 1) / E;
+  g1.a_rows_total = T;
   DSMOE_TRY(dsmoe::launch_grouped_gemm(g1, st));
   DSMOE_MARK(5);
 
@@ -459,6 +461,7 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
   g2.epi = dsmoe::Epilogue::kGateStore;
   g2.row_limit = g2.M_total;
   g2.rows_hint = (T * K + E - 1) / E;
+  g2.a_rows_total = g1.M_total;
   DSMOE_TRY(dsmoe::launch_grouped_gemm(g2, st));
   DSMOE_MARK(6);
 
@@ -480,6 +483,7 @@ dsmoe_status dsmoe_moe_forward(const dsmoe_moe_desc* d, const dsmoe_moe_weights*
     g3.epi = dsmoe::Epilogue::kStore;
     g3.row_limit = T * K + T;
     g3.rows_hint = T;
+    g3.a_rows_total = T * K + T;
     DSMOE_TRY(dsmoe::launch_grouped_gemm(g3, st));
   }
   // y[t] = shared row + routed rows in ascending k (float32 sums)
@@ -780,6 +784,7 @@ dsmoe_status dsmoe_moe_forward_serving(const dsmoe_moe_desc* d, const dsmoe_moe_
   g1.epi = dsmoe::Epilogue::kSwiGLUQuant;
   g1.row_limit = rows;
   g1.rows_hint = hint;
+  g1.a_rows_total = T;
   DSMOE_TRY(dsmoe::launch_grouped_gemm(g1, st));
   DSMOE_MARK(2);
 
@@ -801,6 +806,7 @@ dsmoe_status dsmoe_moe_forward_serving(const dsmoe_moe_desc* d, const dsmoe_moe_
   g2.epi = dsmoe::Epilogue::kGateStore;
   g2.row_limit = rows;
   g2.rows_hint = hint;
+  g2.a_rows_total = rows;
   DSMOE_TRY(dsmoe::launch_grouped_gemm(g2, st));
   DSMOE_MARK(3);
 

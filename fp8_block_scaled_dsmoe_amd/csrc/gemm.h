@@ -34,6 +34,7 @@ struct GemmProblem {
   float* c_scale;            // kSwiGLUQuant: [M_total][N/2/128]
   int64_t row_limit;         // rows >= row_limit are never read or written
   int64_t rows_hint;         // typical rows per group (selects the kernel shape)
+  int64_t a_rows_total;      // rows of A when known (every a_rows entry is below it), else 0
 };
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t s);

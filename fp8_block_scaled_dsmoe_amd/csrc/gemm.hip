@@ -363,6 +363,26 @@ __device__ __forceinline__ void dma_4(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base)
                : "memory", "m0");
 }
+// The same copy through a buffer resource (base and range in SGPRs): the
+// per-lane byte offset voff is a 32-bit VGPR and the wave-uniform soff an
+// SGPR, so a K loop can keep voff fixed and step soff, with no per-copy
+// 64-bit address arithmetic on the VALU.
+typedef int i32x4_rsrc __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_rsrc buffer_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_rsrc r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));   // stride 0
+  r.z = -1;                        // range: every 32-bit offset
+  r.w = 0x00020000;                // raw buffer, 32-bit data format
+  return r;
+}
+__device__ __forceinline__ void dma_16_buf(const i32x4_rsrc& rsrc, uint32_t voff, uint32_t soff,
+                                           uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(lds_base), "s"(soff)
+               : "memory", "m0");
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -574,6 +594,13 @@ constexpr int L2BM = 256;
 #define DSMOE_LDS2 1
 #endif
 constexpr bool kUseLds2 = DSMOE_LDS2 != 0;
+#ifndef DSMOE_LDS2_PRIO
+#define DSMOE_LDS2_PRIO 0
+#endif
+#ifndef DSMOE_LDS2_BUF
+#define DSMOE_LDS2_BUF 1
+#endif
+constexpr bool kLds2Buf = DSMOE_LDS2_BUF != 0;
 
 struct Lds2Cfg {
   static constexpr int THREADS = 512;
@@ -587,7 +614,10 @@ struct Lds2Cfg {
   static_assert(ROWS_PER_WAVE <= 64, "one scale load per lane");
 };
 
-template <Epilogue EPI>
+// kA32: every byte offset into A fits 32 bits (the host knows A's row
+// count), so the A copies use buffer loads with per-lane offsets fixed for
+// the whole K loop.
+template <Epilogue EPI, bool kA32>
 __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n_tiles) {
   using C = Lds2Cfg;
   constexpr int THREADS = C::THREADS;
@@ -630,13 +660,20 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   // copies.  W rows are a uniform base plus lane/8.
   constexpr int A_WAVES = C::A_WLOADS / C::PER_WAVE;
   const bool a_wave = wave < A_WAVES;
+  // (kA32: arow holds the copy's byte offset arow * K + 16 * lseg instead)
   int32_t arow[C::PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::PER_WAVE; ++i) {
     const int row = (wave * C::PER_WAVE + i) * 8 + (lane >> 3);
     const int64_t r = row0 + row < row1 ? row0 + row : row0;
     arow[i] = a_wave ? static_cast<int32_t>(p.a_rows ? p.a_rows[r] : r) : 0;
+    if constexpr (kA32) {
+      const int jj = wave * C::PER_WAVE + i;
+      const int lseg = (lane & 7) ^ (lane >> 3) ^ (jj & 1);
+      arow[i] = static_cast<int32_t>(static_cast<uint32_t>(static_cast<int64_t>(arow[i]) * K + lseg * 16));
+    }
   }
+  const i32x4_rsrc a_rsrc = buffer_rsrc(p.a);
   const int64_t w_lane = static_cast<int64_t>(lane >> 3) * K;
   const float* sa_src;
   {
@@ -650,7 +687,14 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   const uint32_t sa_base = lds_addr(&s_sa[0][0]) + 4 * wave * C::ROWS_PER_WAVE;
 #define DSMOE_ISSUE(cc, st)                                                                  \
   do {                                                                                       \
-    if (a_wave) {                                                                            \
+    if (a_wave && kA32) {                                                                    \
+      _Pragma("unroll") for (int i = 0; i < C::PER_WAVE; ++i) {                              \
+        const int jj = wave * C::PER_WAVE + i;                                               \
+        dma_16_buf(a_rsrc, static_cast<uint32_t>(arow[i]),                                   \
+                   __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((cc) * BK)),          \
+                   __builtin_amdgcn_readfirstlane(st_base + (st) * C::STAGE_BYTES + jj * 1024)); \
+      }                                                                                      \
+    } else if (a_wave) {                                                                     \
       _Pragma("unroll") for (int i = 0; i < C::PER_WAVE; ++i) {                              \
         const int jj = wave * C::PER_WAVE + i;                                               \
         const int lseg = (lane & 7) ^ (lane >> 3) ^ (jj & 1);                                \
@@ -701,6 +745,9 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
     block_barrier();  // everyone's did; everyone is done with chunk c-1 (the other stage)
     if (c + 1 < kchunks) DSMOE_ISSUE(c + 1, buf ^ 1);
     if (nsl > 0) {
+#if DSMOE_LDS2_PRIO
+      __builtin_amdgcn_s_setprio(DSMOE_LDS2_PRIO);
+#endif
       const uint8_t* sa_ = &s_stage[buf][0];
       const uint8_t* sb_ = &s_stage[buf][L2BM * BK];
       const float sw = s_sw[wn][c];
@@ -750,6 +797,9 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
         __builtin_amdgcn_sched_barrier(0);
       }
 #undef DSMOE_BFRAG
+#if DSMOE_LDS2_PRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
     }
   }
 #undef DSMOE_ISSUE
@@ -1149,7 +1199,12 @@ hipError_t launch_lds2(const GemmProblem& p, hipStream_t s) {
   const int64_t n_tiles = (EPI == Epilogue::kSwiGLUQuant) ? (p.N / 2) / 128 : p.N / Lds2Cfg::BN;
   const int64_t blocks = pad_grid(((p.M_total + L2BM - 1) / L2BM + p.G) * n_tiles);
   if (blocks == 0) return hipSuccess;
-  gemm_lds2_kernel<EPI><<<dim3(static_cast<unsigned>(blocks)), Lds2Cfg::THREADS, 0, s>>>(p, n_tiles);
+  // 32-bit A offsets when A's size is known and every row's K bytes fit
+  const bool a32 = kLds2Buf && p.a_rows_total > 0 && p.a_rows_total * p.K <= 0xFFFFFFFFLL;
+  if (a32)
+    gemm_lds2_kernel<EPI, true><<<dim3(static_cast<unsigned>(blocks)), Lds2Cfg::THREADS, 0, s>>>(p, n_tiles);
+  else
+    gemm_lds2_kernel<EPI, false><<<dim3(static_cast<unsigned>(blocks)), Lds2Cfg::THREADS, 0, s>>>(p, n_tiles);
   return hipGetLastError();
 }
 
