@@ -24,7 +24,7 @@ __all__ = [
     "moe_workspace_bytes", "moe_forward", "update_bias", "quantize_layer_weights",
     "quant_rows", "quant_tensor", "gemm_granularity_workspace_bytes", "fp8_gemm_granularity",
     "GRANULARITIES", "plan_replicas", "place_replicas", "place_layer_replicas", "slot_offsets",
-    "moe_serving_workspace_bytes", "moe_forward_serving", "transpose_w_128x128", "BF16", "F32",
+    "moe_serving_workspace_bytes", "moe_forward_serving", "transpose_w_128x128", "e4m3_codes", "BF16", "F32",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsmoe.so")
@@ -112,6 +112,8 @@ lib.dsmoe_place_replicas.restype = _int
 lib.dsmoe_place_replicas.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _vp]
 lib.dsmoe_transpose_w_128x128.restype = _int
 lib.dsmoe_transpose_w_128x128.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]
+lib.dsmoe_e4m3_codes.restype = _int
+lib.dsmoe_e4m3_codes.argtypes = [_vp, _i64, _int, _vp, _vp]
 lib.dsmoe_slot_offsets.restype = _int
 lib.dsmoe_slot_offsets.argtypes = [_vp, _i32, _vp, _vp, _i32, _i64, _vp, _vp]
 lib.dsmoe_moe_serving_workspace_bytes.restype = _sz
@@ -129,7 +131,7 @@ EXPORTED = ("dsmoe_status_str", "dsmoe_abi_version", "dsmoe_quant_act_1x128", "d
             "dsmoe_plan_replicas", "dsmoe_place_replicas", "dsmoe_slot_offsets", "dsmoe_moe_serving_workspace_bytes",
             "dsmoe_moe_forward_serving", "dsmoe_transpose_w_128x128", "dsmoe_moe_forward_noalloc",
             "dsmoe_token_tiles", "dsmoe_quant_tokens_128", "dsmoe_fp8_wgrad_grouped", "dsmoe_swiglu_backward",
-            "dsmoe_gate_backward", "dsmoe_combine_rows")
+            "dsmoe_gate_backward", "dsmoe_combine_rows", "dsmoe_e4m3_codes")
 
 # dsmoe_granularity codes
 GRANULARITIES = {"tensor": 0, "channel": 1, "block": 2}
@@ -215,6 +217,23 @@ def quant_w_128x128(w: torch.Tensor, q: Optional[torch.Tensor] = None,
     if squeeze:
         return q[0], scale[0]
     return q, scale
+
+
+E4M3_CONVERTERS = {"encoder": 0, "packed": 1}
+
+
+def e4m3_codes(x: torch.Tensor, converter: str = "encoder", q: Optional[torch.Tensor] = None):
+    """float32 x (any shape) -> uint8 E4M3FN codes of x at scale 1, from the
+    quantisers' integer encoder ("encoder") or the SwiGLU epilogue's packed
+    conversion ("packed"); see dsmoe_e4m3_codes."""
+    _dev(x, torch.float32, "x")
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if q is None else q
+    _dev(q, torch.uint8, "q")
+    if q.numel() != x.numel():
+        raise ValueError("q must have as many elements as x")
+    _check(lib.dsmoe_e4m3_codes(_p(x), x.numel(), E4M3_CONVERTERS[converter], _p(q), _stream()),
+           "dsmoe_e4m3_codes")
+    return q
 
 
 def transpose_w_128x128(q: torch.Tensor, s: torch.Tensor):

@@ -268,6 +268,17 @@ dsmoe_status dsmoe_quant_w_128x128(const void* w, int wt, int64_t n_mats, int64_
                                              static_cast<hipStream_t>(stream)));
 }
 
+dsmoe_status dsmoe_e4m3_codes(const float* x, int64_t n, int converter, uint8_t* q, void* stream) {
+  if (converter != 0 && converter != 1) return DSMOE_ERR_DTYPE;
+  if (n < 0 || n > (1LL << 40)) return DSMOE_ERR_SHAPE;
+  if (n == 0) return DSMOE_OK;
+  if (!x || !q) return DSMOE_ERR_NULL;
+  if (!aligned(x, 4)) return DSMOE_ERR_ALIGN;
+  const dsmoe_status ds = check_device();
+  if (ds != DSMOE_OK) return ds;
+  return launch_status(dsmoe::launch_e4m3_codes(x, n, converter == 1, q, static_cast<hipStream_t>(stream)));
+}
+
 dsmoe_status dsmoe_transpose_w_128x128(const uint8_t* q, const float* s, int64_t n_mats, int64_t N,
                                        int64_t K, uint8_t* qt, float* st, void* stream) {
   if (n_mats < 0 || N <= 0 || K <= 0 || N % 128 || K % 128) return DSMOE_ERR_SHAPE;

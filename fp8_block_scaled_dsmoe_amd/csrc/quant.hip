@@ -152,6 +152,21 @@ __global__ __launch_bounds__(256) void transpose_blocks_kernel(const uint8_t* __
   if (t == 0) st[mat * kb * nb + bj * nb + bi] = s[mat * nb * kb + bi * kb + bj];
 }
 
+// Unit-scale codes of n floats, two per thread: HW = false runs the integer
+// encoder the quantisers use, HW = true the packed conversion of the SwiGLU
+// epilogue.
+template <bool HW>
+__global__ __launch_bounds__(256) void e4m3_codes_kernel(const float* __restrict__ x, int64_t n,
+                                                         uint8_t* __restrict__ q) {
+  const int64_t i = 2 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
+  if (i >= n) return;
+  const float a = x[i];
+  const float b = i + 1 < n ? x[i + 1] : 0.0f;
+  const uint32_t c = HW ? e4m3_encode2(a, b) : (e4m3_encode(a) | (e4m3_encode(b) << 8));
+  q[i] = static_cast<uint8_t>(c & 0xFFu);
+  if (i + 1 < n) q[i + 1] = static_cast<uint8_t>(c >> 8);
+}
+
 }  // namespace
 
 hipError_t launch_quant_act(const void* x, bool x_f32, int64_t rows, int64_t cols, uint8_t* q,
@@ -163,6 +178,16 @@ hipError_t launch_quant_act(const void* x, bool x_f32, int64_t rows, int64_t col
     quant_act_kernel<true><<<grid, 256, 0, s>>>(x, n_tiles, q, scale);
   else
     quant_act_kernel<false><<<grid, 256, 0, s>>>(x, n_tiles, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_e4m3_codes(const float* x, int64_t n, bool hw, uint8_t* q, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((n + 511) / 512));
+  if (hw)
+    e4m3_codes_kernel<true><<<grid, 256, 0, s>>>(x, n, q);
+  else
+    e4m3_codes_kernel<false><<<grid, 256, 0, s>>>(x, n, q);
   return hipGetLastError();
 }
 

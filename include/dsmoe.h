@@ -104,6 +104,23 @@ dsmoe_status dsmoe_quant_w_128x128(const void* w, int wt, int64_t n_mats, int64_
                                    uint8_t* q, float* scale, void* stream);
 
 /*
+ * dsmoe_e4m3_codes -- E4M3FN codes of floats taken as already scaled (scale
+ * 1), with either of the two encoders the kernels use.  Source: V3 notes §6
+ * and infra answer, FP8 paragraph (E4M3 for every FP8 tensor); the rounding
+ * rule is that of dsmoe_quant_act_1x128.
+ *
+ *   x          [n] float32
+ *   converter  0: the integer encoder of the quantisers; 1: gfx950's packed
+ *              conversion with the inputs clamped to +-448 first (the SwiGLU
+ *              epilogue's).  Both round to nearest with ties to even,
+ *              saturate at +-448 and keep the sign of zero; NaN inputs have
+ *              no defined code.
+ *   q          [n] uint8 codes (output)
+ * Requires n >= 0; a converter other than 0 or 1 gives DSMOE_ERR_DTYPE.
+ */
+dsmoe_status dsmoe_e4m3_codes(const float* x, int64_t n, int converter, uint8_t* q, void* stream);
+
+/*
  * dsmoe_transpose_w_128x128 -- the weight operand of a data-gradient GEMM.
  * Source: V3 notes §6 (the activation-gradient GEMM runs in FP8 like the
  * forward) and §6.1 (128x128 weight blocks).  A block's amax does not change

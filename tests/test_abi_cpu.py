@@ -20,7 +20,7 @@ def _declared():
 def test_library_exports_every_declared_function():
     import fp8_block_scaled_dsmoe_amd as d
     names = _declared()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     for n in names:
         assert hasattr(d.lib, n), f"{n} not exported"
     assert sorted(d.EXPORTED) == names
@@ -76,6 +76,11 @@ def test_quant_validation_errors():
     assert L.dsmoe_transpose_w_128x128(a, a, 1, 128, 128, None, a, None) == 1
     assert L.dsmoe_transpose_w_128x128(a, a, 1, 128, 128, _vp(MISALIGNED), a, None) == 3
     assert L.dsmoe_transpose_w_128x128(None, None, 0, 128, 128, None, None, None) == 0
+    assert L.dsmoe_e4m3_codes(a, 8, 2, a, None) == 4                 # unknown converter
+    assert L.dsmoe_e4m3_codes(a, -1, 0, a, None) == 2
+    assert L.dsmoe_e4m3_codes(None, 8, 1, a, None) == 1
+    assert L.dsmoe_e4m3_codes(_vp(MISALIGNED), 8, 0, a, None) == 3
+    assert L.dsmoe_e4m3_codes(None, 0, 1, None, None) == 0           # empty: no-op
 
 
 def test_granularity_validation_errors():

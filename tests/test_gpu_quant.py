@@ -168,3 +168,61 @@ def test_codes_near_rounding_points_with_a_general_scale(amax):
     q, s, _ = d.quant_tensor(dev(x, torch.float32))
     qo, so = og.quant_tensor(x)
     assert host(s)[0] == so and np.array_equal(host(q), qo)
+
+
+def _codes_from_midpoints(absv: torch.Tensor, mids: torch.Tensor) -> torch.Tensor:
+    """Code magnitudes of |v| from the sorted midpoints of neighbouring E4M3
+    magnitudes: the number of midpoints below |v|, moved up to the even code
+    where |v| sits exactly on a midpoint (ties to even: the low bit of a code
+    is the low bit of its mantissa); 126 (0x7E, 448) for everything above
+    the last midpoint."""
+    n = torch.bucketize(absv, mids)                   # midpoints strictly below |v|
+    on_mid = (n < mids.numel()) & (absv == mids[n.clamp(max=mids.numel() - 1)])
+    return (n + (on_mid & (n % 2 == 1)).to(n.dtype)).to(torch.uint8)
+
+
+def test_every_float_up_to_464_encodes_to_the_codes_the_midpoints_give():
+    """Every float32 with |v| <= 464, both signs (2.28e9 values), through both
+    encoders at scale 1 (dsmoe_e4m3_codes): the quantisers' integer encoder
+    and the SwiGLU epilogue's packed conversion must give the code the
+    oracle's 126 midpoints give (464 is the tie between 448 and the step
+    past it, which goes to 448; beyond 448 both saturate)."""
+    d = _dsmoe()
+    from oracle import e4m3
+    mags = e4m3.decode(np.arange(0, 127, dtype=np.uint8))          # 0 .. 448, increasing
+    mids64 = (mags[:-1] + mags[1:]) / 2
+    assert mids64.size == 126 and np.all(np.diff(mids64) > 0)
+    mids32 = mids64.astype(np.float32)
+    assert np.array_equal(mids32.astype(np.float64), mids64)      # exact in float32
+    # the rule above agrees with the oracle's encoder on the midpoints and their neighbours
+    probe = np.concatenate([mids32, np.nextafter(mids32, np.float32(0)), np.nextafter(mids32, np.float32(1e9)),
+                            np.float32([0.0, 448.0, 460.0, 464.0])])
+    want_probe = e4m3.encode(probe)
+    got_probe = _codes_from_midpoints(torch.from_numpy(probe), torch.from_numpy(mids32)).numpy()
+    assert np.array_equal(got_probe, want_probe)
+    mids = torch.from_numpy(mids32).cuda()
+    top = int(np.float32(464.0).view(np.uint32))                  # 0x43E80000
+    chunk = 1 << 28
+    banner(f"e4m3 sweep of every float32 with |v| <= 464 ({2 * (top + 1)} values)")
+    checked = 0
+    for start in range(0, top + 1, chunk):
+        end = min(top + 1, start + chunk)
+        bits = torch.arange(start, end, dtype=torch.int32, device="cuda")
+        pos = bits.view(torch.float32)
+        want_mag = _codes_from_midpoints(pos, mids)
+        for sign, x in ((0, pos), (0x80, -pos)):                  # negation flips only the sign bit
+            want = want_mag | sign
+            for conv in ("encoder", "packed"):
+                q = d.e4m3_codes(x, conv)
+                bad = (q != want).nonzero()
+                if bad.numel():
+                    i = int(bad[0, 0])
+                    raise AssertionError(
+                        f"{conv}: {bad.numel()} codes differ in bits [{start:#x}, {end:#x}) sign {sign:#x}; "
+                        f"first: v={float(x[i])!r} (bits {int(bits[i]):#x}) gpu {int(q[i]):#04x} "
+                        f"want {int(want[i]):#04x}")
+            checked += end - start
+        del bits, pos, want_mag
+    torch.cuda.synchronize()
+    assert checked == 2 * (top + 1)
+    print(f"[parity] e4m3 sweep: {checked} values, both encoders, every code as the midpoints give", flush=True)
