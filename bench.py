@@ -216,6 +216,16 @@ def imbalance(counts):
             "zero_load_experts": int((c == 0).sum())}
 
 
+def row_tile_fill(counts, T):
+    """Rows of the gate/up GEMM's groups (the routed experts' counts, then the
+    shared expert's T rows) over the rows of the row tiles covering them, for
+    the 256-row tiles of the MFMA-bound kernel: the share of its MFMA row
+    slots that hold a row."""
+    import numpy as np
+    rows = np.append(np.asarray(counts, np.int64), T)
+    return round(float(rows.sum() / (np.ceil(rows / 256) * 256).sum()), 4)
+
+
 def routing_trajectory(d, torch, logits, bias_init, cfg, n_steps):
     """Imbalance along n_steps aux-loss-free bias updates with routing only
     (dsmoe_route + dsmoe_update_bias on the batch's fixed logits), at a few
@@ -883,6 +893,7 @@ def main():
         "layer_frac_hbm_peak": round(layer_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "layer_algorithmic_bytes": int(layer_bytes),
         "experts_touched": touched,
+        "row_tile_fill": row_tile_fill(counts_last, T),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "quant_w_ms": round(quant_w_ms, 3),
         "load_balance": dict(balance, last_timed_step=imbalance(counts_last)),

@@ -383,6 +383,11 @@ __device__ __forceinline__ void dma_16_buf(const i32x4_rsrc& rsrc, uint32_t voff
                "s"(lds_base), "s"(soff)
                : "memory", "m0");
 }
+__device__ __forceinline__ void dma_4_buf(const i32x4_rsrc& rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(lds_base)
+               : "memory", "m0");
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -594,9 +599,6 @@ constexpr int L2BM = 256;
 #define DSMOE_LDS2 1
 #endif
 constexpr bool kUseLds2 = DSMOE_LDS2 != 0;
-#ifndef DSMOE_LDS2_PRIO
-#define DSMOE_LDS2_PRIO 0
-#endif
 #ifndef DSMOE_LDS2_BUF
 #define DSMOE_LDS2_BUF 1
 #endif
@@ -609,9 +611,14 @@ struct Lds2Cfg {
   static constexpr int A_WLOADS = L2BM * BK / 1024;   // 32 wave-loads of 1 KB per chunk
   static constexpr int B_WLOADS = BN * BK / 1024;     // 32
   static constexpr int PER_WAVE = (A_WLOADS + B_WLOADS) / NW;
-  static constexpr int ROWS_PER_WAVE = L2BM / NW;      // 1x128 scales staged per wave
   static constexpr int STAGE_BYTES = (L2BM + BN) * BK;
-  static_assert(ROWS_PER_WAVE <= 64, "one scale load per lane");
+  // A's 1x128 scales are staged SA_BLOCK = 8 chunks at a time: lane l of a
+  // copy takes row l / 8 (the row of the wave's A copy with the same index)
+  // and chunk l % 8, so the lanes of one row read its contiguous run of
+  // scales (the layout is [rows][chunks]).  One copy per chunk would read one
+  // scale from each of 32 rows, 32 cache lines for 128 bytes, and such copies
+  // took longer than the A and W copies together.
+  static constexpr int SA_BLOCK = 8;
 };
 
 // kA32: every byte offset into A fits 32 bits (the host knows A's row
@@ -623,7 +630,7 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   constexpr int THREADS = C::THREADS;
   constexpr int BN = C::BN;
   __shared__ __attribute__((aligned(1024))) uint8_t s_stage[2][C::STAGE_BYTES];   // [A | W] per stage
-  __shared__ __attribute__((aligned(256))) float s_sa[2][L2BM];
+  __shared__ __attribute__((aligned(256))) float s_sa[2][L2BM * C::SA_BLOCK];   // [row][chunk % 8]
   __shared__ float s_sw[2][kMaxChunks];
   __shared__ int64_t s_scan[THREADS / 64];
   __shared__ int64_t s_tile[4];
@@ -650,72 +657,83 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   const int64_t w_up_shift = (EPI == Epilogue::kSwiGLUQuant) ? N / 2 - 128 : 0;
 #define DSMOE_WROW(lc) (w_row_base + (lc) + ((lc) >= 128 ? w_up_shift : 0))
 
-  // Waves 0-3 copy the A chunk, waves 4-7 the W chunk: wave-load jj covers
-  // tile rows 8jj .. 8jj+7 (lane -> row 8jj + lane/8, physical segment lane%8
-  // holding logical segment (lane%8) ^ swz_key(row); swz_key(row) is
-  // (lane/8) ^ (jj & 1) for these rows).  A waves keep the gathered row of
-  // each of their loads (32-bit) and form the 64-bit address at issue time:
-  // eight precomputed addresses did not fit, and reloading a spilled one
-  // waits for every outstanding copy (vmcnt(0)), serialising the chunk's
-  // copies.  W rows are a uniform base plus lane/8.
-  constexpr int A_WAVES = C::A_WLOADS / C::PER_WAVE;
-  const bool a_wave = wave < A_WAVES;
-  // (kA32: arow holds the copy's byte offset arow * K + 16 * lseg instead)
-  int32_t arow[C::PER_WAVE];
+  // Every wave copies 4 of the chunk's 32 A wave-loads and 4 of its 32 W
+  // wave-loads: wave-load jj covers tile rows 8jj .. 8jj+7 (lane -> row
+  // 8jj + lane/8, physical segment lane%8 holding logical segment
+  // (lane%8) ^ swz_key(row); swz_key(row) is (lane/8) ^ (jj & 1) for these
+  // rows).  A copies keep the gathered row of each load (32-bit) and form the
+  // address at issue time (kA32: the byte offset row * K + 16 * lseg, fixed
+  // over the K loop); W copies are a wave-uniform row offset plus one of two
+  // per-lane offsets (by the parity of jj), all through buffer resources.
+  constexpr int CP = C::PER_WAVE / 2;   // A (and W) copies per wave
+  static_assert(C::PER_WAVE == 8 && C::A_WLOADS == C::NW * CP && C::B_WLOADS == C::NW * CP,
+                "a chunk's copies are spread over 5 + 3 MFMA steps");
+  int32_t arow[CP];
 #pragma unroll
-  for (int i = 0; i < C::PER_WAVE; ++i) {
-    const int row = (wave * C::PER_WAVE + i) * 8 + (lane >> 3);
+  for (int i = 0; i < CP; ++i) {
+    const int row = (wave * CP + i) * 8 + (lane >> 3);
     const int64_t r = row0 + row < row1 ? row0 + row : row0;
-    arow[i] = a_wave ? static_cast<int32_t>(p.a_rows ? p.a_rows[r] : r) : 0;
+    arow[i] = static_cast<int32_t>(p.a_rows ? p.a_rows[r] : r);
     if constexpr (kA32) {
-      const int jj = wave * C::PER_WAVE + i;
-      const int lseg = (lane & 7) ^ (lane >> 3) ^ (jj & 1);
+      const int lseg = (lane & 7) ^ (lane >> 3) ^ (i & 1);
       arow[i] = static_cast<int32_t>(static_cast<uint32_t>(static_cast<int64_t>(arow[i]) * K + lseg * 16));
     }
   }
   const i32x4_rsrc a_rsrc = buffer_rsrc(p.a);
-  const int64_t w_lane = static_cast<int64_t>(lane >> 3) * K;
-  const float* sa_src;
-  {
-    const int row = wave * C::ROWS_PER_WAVE + (lane < C::ROWS_PER_WAVE ? lane : 0);
-    const int64_t r = row0 + row < row1 ? row0 + row : row0;
-    const int64_t sr = p.a_rows ? p.a_rows[r] : r;
-    sa_src = p.a_scale + sr * kchunks;
-  }
-
+  const i32x4_rsrc w_rsrc = buffer_rsrc(wbase);
+  uint32_t w_voff[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    w_voff[par] = static_cast<uint32_t>((lane >> 3) * K + (((lane & 7) ^ (lane >> 3) ^ par) << 4));
   const uint32_t st_base = lds_addr(&s_stage[0][0]);
-  const uint32_t sa_base = lds_addr(&s_sa[0][0]) + 4 * wave * C::ROWS_PER_WAVE;
-#define DSMOE_ISSUE(cc, st)                                                                  \
+  const uint32_t sa_base = lds_addr(&s_sa[0][0]);
+  const i32x4_rsrc sa_rsrc = buffer_rsrc(p.a_scale);
+  // Each wave also copies the scales of chunks [8 blk, 8 blk + 8) of the rows
+  // of its A copies into s_sa[blk & 1] (chunks past the end repeat the last
+  // one): copy i covers rows 8 (4w + i) + lane / 8, whose scale row starts
+  // arow[i] * kchunks scales in (kA32: arow[i] / 128, since the byte offset
+  // is row * K plus less than 128).
+#define DSMOE_ISSUE_SA(blk)                                                                  \
   do {                                                                                       \
-    if (a_wave && kA32) {                                                                    \
-      _Pragma("unroll") for (int i = 0; i < C::PER_WAVE; ++i) {                              \
-        const int jj = wave * C::PER_WAVE + i;                                               \
+    const int ch_ = min(static_cast<int>(blk) * C::SA_BLOCK + lane % C::SA_BLOCK,            \
+                        static_cast<int>(kchunks) - 1);                                      \
+    _Pragma("unroll") for (int i = 0; i < CP; ++i) {                                         \
+      const uint32_t ld_ = __builtin_amdgcn_readfirstlane(                                   \
+          sa_base + ((blk) & 1) * (L2BM * C::SA_BLOCK * 4) + (wave * CP + i) * 256);         \
+      if constexpr (kA32)                                                                    \
+        dma_4_buf(sa_rsrc, ((static_cast<uint32_t>(arow[i]) >> 7) + ch_) * 4, ld_);          \
+      else                                                                                   \
+        dma_4(p.a_scale + static_cast<int64_t>(arow[i]) * kchunks + ch_, ld_);               \
+    }                                                                                        \
+  } while (0)
+// copy i (of PER_WAVE: A copies 0-3, W copies 4-7) of this wave for chunk cc
+// into stage st
+#define DSMOE_ISSUE1(cc, st, i)                                                              \
+  do {                                                                                       \
+    if ((i) < CP) {                                                                          \
+      const int jj = wave * CP + (i);                                                        \
+      if constexpr (kA32) {                                                                  \
         dma_16_buf(a_rsrc, static_cast<uint32_t>(arow[i]),                                   \
                    __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((cc) * BK)),          \
                    __builtin_amdgcn_readfirstlane(st_base + (st) * C::STAGE_BYTES + jj * 1024)); \
-      }                                                                                      \
-    } else if (a_wave) {                                                                     \
-      _Pragma("unroll") for (int i = 0; i < C::PER_WAVE; ++i) {                              \
-        const int jj = wave * C::PER_WAVE + i;                                               \
-        const int lseg = (lane & 7) ^ (lane >> 3) ^ (jj & 1);                                \
+      } else {                                                                               \
+        const int lseg = (lane & 7) ^ (lane >> 3) ^ ((i) & 1);                               \
         int32_t ar = arow[i];                                                                \
         asm volatile("" : "+v"(ar));  /* address formed here, not kept live across chunks */ \
         dma_16(p.a + static_cast<int64_t>(ar) * K + (cc) * BK + lseg * 16,                   \
                __builtin_amdgcn_readfirstlane(st_base + (st) * C::STAGE_BYTES + jj * 1024)); \
       }                                                                                      \
     } else {                                                                                 \
-      _Pragma("unroll") for (int i = 0; i < C::PER_WAVE; ++i) {                              \
-        const int jj = (wave - A_WAVES) * C::PER_WAVE + i;                                   \
-        const int lseg = (lane & 7) ^ (lane >> 3) ^ (jj & 1);                                \
-        const int64_t wr0 = w_row_base + jj * 8 + (jj * 8 >= 128 ? w_up_shift : 0);          \
-        const uint8_t* wrow = wbase + wr0 * K + (cc) * BK;  /* wave-uniform */                \
-        asm volatile("" : "+s"(wrow));  /* formed here (scalar), not kept per lane */          \
-        dma_16(wrow + w_lane + lseg * 16,                                                    \
-               __builtin_amdgcn_readfirstlane(st_base + (st) * C::STAGE_BYTES + L2BM * BK + jj * 1024)); \
-      }                                                                                      \
+      const int jj = wave * CP + (i) - CP;                                                   \
+      const int64_t wr0 = w_row_base + jj * 8 + (jj * 8 >= 128 ? w_up_shift : 0);            \
+      dma_16_buf(w_rsrc, w_voff[(i) & 1],                                                    \
+                 __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(wr0 * K + (cc) * BK)),  \
+                 __builtin_amdgcn_readfirstlane(st_base + (st) * C::STAGE_BYTES + L2BM * BK + jj * 1024)); \
     }                                                                                        \
-    if (lane < C::ROWS_PER_WAVE)                                                             \
-      dma_4(sa_src + (cc), __builtin_amdgcn_readfirstlane(sa_base + (st) * (L2BM * 4)));      \
+  } while (0)
+#define DSMOE_ISSUE(cc, st)                                                                  \
+  do {                                                                                       \
+    _Pragma("unroll") for (int i_ = 0; i_ < C::PER_WAVE; ++i_) DSMOE_ISSUE1(cc, st, i_);     \
   } while (0)
 
   f32x4 acc[4][8];
@@ -732,6 +750,7 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   // chunk 0's copies first: they need no staged scale, so their latency
   // overlaps the weight-block scale staging and its barrier
   DSMOE_ISSUE(0, 0);
+  DSMOE_ISSUE_SA(0);
   for (int64_t i = tid; i < 2 * kchunks; i += THREADS) {
     const int hb = static_cast<int>(i / kchunks);
     const int64_t c = i - hb * kchunks;
@@ -739,70 +758,154 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   }
 #undef DSMOE_WROW
   __syncthreads();
-  for (int64_t c = 0; c < kchunks; ++c) {
-    const int buf = static_cast<int>(c & 1);
-    wait_vmcnt<0>();  // this wave's copies of chunk c landed
-    block_barrier();  // everyone's did; everyone is done with chunk c-1 (the other stage)
-    if (c + 1 < kchunks) DSMOE_ISSUE(c + 1, buf ^ 1);
-    if (nsl > 0) {
-#if DSMOE_LDS2_PRIO
-      __builtin_amdgcn_s_setprio(DSMOE_LDS2_PRIO);
-#endif
-      const uint8_t* sa_ = &s_stage[buf][0];
-      const uint8_t* sb_ = &s_stage[buf][L2BM * BK];
-      const float sw = s_sw[wn][c];
-      i32x8 fa[4];
-      float scl[4][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + frow;
-        fa[i] = cat8(*reinterpret_cast<const u32x4*>(sa_ + swz(r, fseg)),
-                     *reinterpret_cast<const u32x4*>(sa_ + swz(r, fseg + 1)));
-        const f32x4 s4 = *reinterpret_cast<const f32x4*>(&s_sa[buf][wm * 64 + i * 16 + (lane >> 4) * 4]);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) scl[i][rr] = s4[rr] * sw;
-      }
-      i32x8 bf[2];
-      f32x4 part[3];
-#define DSMOE_BFRAG(jj)                                                                        \
+  wait_vmcnt<0>();  // this wave's copies of chunk 0 landed
+  block_barrier();  // everyone's did
+  if (kchunks > 1) DSMOE_ISSUE(1, 1);
+
+  // The MFMAs of all chunks form one stream: chunk c's 32 MFMAs run as
+  // k = 4j + i (W fragment j, row slice i); step k issues MFMA k and
+  // promotes MFMA k-2 (for k < 2 the last two of the previous chunk), whose
+  // result the MFMA in between covers; partial sums rotate through four
+  // register sets, so the ring lines up across chunks.  W fragment j+1 is
+  // read at the start of column j.  The barrier sits after step 26, once the
+  // wave has read its last fragment of the chunk's stage: past it the stage
+  // is refilled with chunk c+2 while the last column's MFMAs run, and each of
+  // them is followed by the read of the next chunk's fragment for the same
+  // row slice (and that slice's row scales), so the next chunk starts with
+  // its operands in registers instead of with every wave reading LDS at once.
+  i32x8 fa[4], bf[2];
+  f32x4 part[4];
+  float scl[4][4];
+  f32x4 s4n[4];
+  float swn;
+  const uint8_t* st0 = &s_stage[0][0];
+#define DSMOE_RD_A(i_, stp)                                                                    \
+  do {                                                                                         \
+    const int r_ = wm * 64 + (i_) * 16 + frow;                                                 \
+    fa[i_] = cat8(*reinterpret_cast<const u32x4*>((stp) + swz(r_, fseg)),                     \
+                  *reinterpret_cast<const u32x4*>((stp) + swz(r_, fseg + 1)));                \
+  } while (0)
+#define DSMOE_RD_B(jj, stp)                                                                    \
   do {                                                                                         \
     const int r_ = wn * 128 + (jj) * 16 + frow;                                                \
-    bf[(jj) & 1] = cat8(*reinterpret_cast<const u32x4*>(sb_ + swz(r_, fseg)),                  \
-                        *reinterpret_cast<const u32x4*>(sb_ + swz(r_, fseg + 1)));             \
+    bf[(jj) & 1] = cat8(*reinterpret_cast<const u32x4*>((stp) + L2BM * BK + swz(r_, fseg)),   \
+                        *reinterpret_cast<const u32x4*>((stp) + L2BM * BK + swz(r_, fseg + 1))); \
   } while (0)
-      // The chunk's 32 MFMAs in one sequence k = 4j + i (W fragment j, row
-      // slice i); step k issues MFMA k and promotes MFMA k-2, whose result
-      // two MFMAs (64 cycles of the matrix pipe) cover; partial sums rotate
-      // through three register sets.  W fragment j+1 is read at the start of
-      // column j.
-      DSMOE_BFRAG(0);
+  // row scales of chunk cc for row slice i_ (4 rows per lane)
+#define DSMOE_RD_S(i_, cc)                                                                     \
+  do {                                                                                         \
+    const float* sp_ = &s_sa[((cc) / C::SA_BLOCK) & 1][(wm * 64 + (i_) * 16 + (lane >> 4) * 4) * C::SA_BLOCK + \
+                                                        (cc) % C::SA_BLOCK];                   \
+    _Pragma("unroll") for (int rr = 0; rr < 4; ++rr) s4n[i_][rr] = sp_[rr * C::SA_BLOCK];      \
+  } while (0)
+#define DSMOE_SCL(i_)                                                  \
+  do {                                                                 \
+    _Pragma("unroll") for (int rr = 0; rr < 4; ++rr) scl[i_][rr] = s4n[i_][rr] * swn; \
+  } while (0)
+  // one step: MFMA k, then the promotion of MFMA k-2 (ring slot (k-2) & 3)
+#define DSMOE_STEP(k, stp)                                                                     \
+  do {                                                                                         \
+    const int j_ = (k) >> 2, i_ = (k) & 3;                                                     \
+    if (i_ == 0 && j_ + 1 < 8) DSMOE_RD_B(j_ + 1, stp);                                        \
+    part[(k) & 3] = mfma_chunk(fa[i_], bf[j_ & 1]);                                            \
+    const int kp_ = ((k) + 30) & 31, jp_ = kp_ >> 2, ip_ = kp_ & 3;                            \
+    _Pragma("unroll") for (int rr = 0; rr < 4; ++rr)                                           \
+      acc[ip_][jp_][rr] = __builtin_fmaf(part[kp_ & 3][rr], scl[ip_][rr], acc[ip_][jp_][rr]); \
+  } while (0)
+  // per step: the MFMA, then its LDS reads, then its VALU work (a step
+  // has at most 6 reads and 8 VALU instructions)
+#define DSMOE_SCHED()                                                  \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   \
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                   \
+  __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);                   \
+  __builtin_amdgcn_sched_barrier(0)
+
+  // chunk 0's operands; the promotions of steps 0 and 1 (the previous
+  // chunk's last MFMAs, of which there are none) add 0 * 0
+  part[2] = part[3] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < 34; ++k) {
-        const int j = k >> 2, i = k & 3;
-        if (k < 32) {
-          if (i == 0 && j + 1 < 8) DSMOE_BFRAG(j + 1);
-          part[k % 3] = mfma_chunk(fa[i], bf[j & 1]);
-        }
-        if (k >= 2) {
-          const int kp = k - 2, jp = kp >> 2, ip = kp & 3;
-          {
+  for (int rr = 0; rr < 4; ++rr) scl[2][rr] = scl[3][rr] = 0.f;
+  if (nsl > 0) {
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-              acc[ip][jp][rr] = __builtin_fmaf(part[kp % 3][rr], scl[ip][rr], acc[ip][jp][rr]);
+    for (int i = 0; i < 4; ++i) {
+      DSMOE_RD_A(i, st0);
+      DSMOE_RD_S(i, 0);
+    }
+    DSMOE_RD_B(0, st0);
+    swn = s_sw[wn][0];
+    DSMOE_SCL(0);
+    DSMOE_SCL(1);
+  }
+
+  for (int64_t c = 0; c < kchunks; ++c) {
+    const int buf = static_cast<int>(c & 1);
+    const uint8_t* stc = st0 + buf * C::STAGE_BYTES;          // chunk c
+    const uint8_t* stn = st0 + (buf ^ 1) * C::STAGE_BYTES;    // chunk c + 1
+    // Copies are spread over the MFMA steps, one per step: a wave that
+    // issued all of a chunk's copies at once waited at issue for the address
+    // unit, with its MFMAs queued behind them.  Chunk c+2's copies 0-4 go out
+    // at steps 27-31 of chunk c and copies 5-7 at steps 0-2 of chunk c+1.
+    // They are issued unconditionally (no branch in the MFMA stream) with the
+    // chunk index clamped to the last chunk: a copy past the end (and chunk
+    // 1's copies 5-7, which went out before the loop) rewrites a stage no
+    // later step reads, or writes the same bytes again before the barrier.
+    const int64_t c_prev = c + 1 < kchunks ? c + 1 : kchunks - 1;   // copies 5-7 of chunk c+1
+    const int64_t c_next = c + 2 < kchunks ? c + 2 : kchunks - 1;   // copies 0-4 of chunk c+2
+    if (nsl > 0) {
+#pragma unroll
+      for (int k = 0; k < 27; ++k) {
+        DSMOE_STEP(k, stc);
+        if (k == 0) DSMOE_SCL(2);   // after the promotion of the previous chunk's MFMA 30
+        if (k == 1) DSMOE_SCL(3);
+        if (k < C::PER_WAVE - 5) DSMOE_ISSUE1(c_prev, buf ^ 1, 5 + k);
+        DSMOE_SCHED();
+      }
+    }
+    // every wave has read its last fragment of chunk c's stage (W fragment 7,
+    // step 24) and its copies of chunk c+1 have landed
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    block_barrier();
+    if (c + 2 < kchunks) {
+      if (nsl == 0) DSMOE_ISSUE(c + 2, buf);   // no MFMAs to spread them over
+      if ((c + 2) % C::SA_BLOCK == 0) DSMOE_ISSUE_SA((c + 2) / C::SA_BLOCK);
+    }
+    if (nsl > 0) {
+      const float* swp = &s_sw[wn][c + 1 < kchunks ? c + 1 : c];
+#pragma unroll
+      for (int k = 27; k < 32; ++k) {
+        DSMOE_STEP(k, stc);
+        DSMOE_ISSUE1(c_next, buf, k - 27);
+        if (k >= 28) {   // fa[k-28] had its last use in MFMA k
+          DSMOE_RD_A(k - 28, stn);
+          DSMOE_RD_S(k - 28, c + 1);
+          if (k == 28) {
+            DSMOE_RD_B(0, stn);
+            swn = *swp;
           }
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
-        __builtin_amdgcn_sched_barrier(0);
+        if (k == 30) DSMOE_SCL(0);  // after the promotion of MFMA 28
+        if (k == 31) DSMOE_SCL(1);
+        DSMOE_SCHED();
       }
-#undef DSMOE_BFRAG
-#if DSMOE_LDS2_PRIO
-      __builtin_amdgcn_s_setprio(0);
-#endif
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the copies past the end landed
+  if (nsl > 0) {   // the last chunk's MFMAs 30 and 31
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      acc[2][7][rr] = __builtin_fmaf(part[2][rr], scl[2][rr], acc[2][7][rr]);
+      acc[3][7][rr] = __builtin_fmaf(part[3][rr], scl[3][rr], acc[3][7][rr]);
+    }
+  }
+#undef DSMOE_RD_A
+#undef DSMOE_RD_B
+#undef DSMOE_RD_S
+#undef DSMOE_SCL
+#undef DSMOE_STEP
+#undef DSMOE_SCHED
 #undef DSMOE_ISSUE
+#undef DSMOE_ISSUE1
+#undef DSMOE_ISSUE_SA
   __syncthreads();  // all waves are done with the stages (the epilogues reuse them)
 
   if constexpr (EPI != Epilogue::kSwiGLUQuant) {
@@ -1366,7 +1469,8 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t s) {
       case Epilogue::kSwiGLUQuant: return launch_ws_bm<Epilogue::kSwiGLUQuant>(p, bm, s);
     }
   }
-  if (kUseLds2 && wide) {
+  // (the 256 x 256 kernel addresses a weight matrix with 32-bit offsets)
+  if (kUseLds2 && wide && p.N * p.K <= 0xFFFFFFFFLL) {
     switch (p.epi) {
       case Epilogue::kStore: return launch_lds2<Epilogue::kStore>(p, s);
       case Epilogue::kGateStore: return launch_lds2<Epilogue::kGateStore>(p, s);

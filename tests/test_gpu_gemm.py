@@ -48,7 +48,10 @@ def test_golden_two_chunk(golden):
         assert np.all(ch[0, 1:] == 0)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (300, 384, 640), (129, 256, 1024), (1000, 512, 256)])
+# (700, 256, 128) and (513, 768, 384): the 256 x 256 kernel with one and
+# three K chunks (its stage ring and cross-chunk pipeline at their shortest)
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (300, 384, 640), (129, 256, 1024), (1000, 512, 256),
+                                   (700, 256, 128), (513, 768, 384)])
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
 def test_dense_random_codes(M, N, K, dt):
     d = _dsmoe()
