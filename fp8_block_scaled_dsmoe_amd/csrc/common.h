@@ -61,6 +61,24 @@ __device__ __forceinline__ uint32_t e4m3_encode2(float a, float b) {
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
 }
 
+// E4M3 codes (low byte, next byte) of the IEEE quotients a / sa and b / sb
+// from reciprocals ra = fl(1 / sa) and rb = fl(1 / sb) (IEEE divisions):
+// q = fl(a * ra) is within 2^-23 (relative) of a / sa, so the quotient lies
+// strictly between fl(q * (1 - 2^-22)) and fl(q * (1 + 2^-22)) (for q a
+// normal float; a smaller q and its quotient both encode to a signed zero).
+// The encoder is monotone, so where both ends give one code it is the
+// quotient's; the function returns the lower end's codes and sets `unsure`
+// where the ends differ (a few ulps from a rounding point, or across zero)
+// or a reciprocal overflowed: there the caller encodes the quotient itself.
+__device__ __forceinline__ uint32_t e4m3_encode2_recip(float a, float b, float ra, float rb, bool& unsure) {
+  constexpr float kBelow = 1.0f - 0x1p-22f, kAbove = 1.0f + 0x1p-22f;
+  const float qa = a * ra, qb = b * rb;
+  const uint32_t lo = e4m3_encode2(qa * kBelow, qb * kBelow);
+  const uint32_t hi = e4m3_encode2(qa * kAbove, qb * kAbove);
+  unsure = unsure || lo != hi || !(ra < 0x1p127f) || !(rb < 0x1p127f);
+  return lo;
+}
+
 // ---------------------------------------------------------------------------
 // Wave helpers
 // ---------------------------------------------------------------------------

@@ -236,12 +236,15 @@ __device__ __forceinline__ void epi_rows(const GemmProblem& p, const f32x4 (&acc
 // the NSLOTS waves that share the row through s_rmax by one thread per row,
 // which also forms scale = amax / 448 (IEEE division), stores it and leaves
 // it for the code pass: code = E4M3(a / scale) from the IEEE quotient, as in
-// the standalone quantisers, by the hardware conversion.  The codes are
-// stored with 16-byte writes.
+// the standalone quantisers, by the hardware conversion.  The quotient's code
+// comes from a * (1 / scale) and its bracket (e4m3_encode2_recip), with the
+// division done only by a wave that has a value the bracket leaves unsure.
+// The codes are stored with 16-byte writes.
 //   s_ex:   [pairs][2][NI][NJ/2][64 lanes] f32x4
 //   s_rmax: [NSLOTS][ROWS] f32
-//   s_code: [ROWS][128] bytes
-template <int NI, int NJ, int ROWS, int NSLOTS>
+//   s_code: [ROWS][CS] bytes (CS >= 128; a padded stride spreads the byte writes of
+//           rows 4 apart over more banks)
+template <int NI, int NJ, int ROWS, int NSLOTS, int CS = 128>
 __device__ __forceinline__ void epi_swiglu(const GemmProblem& p, const f32x4 (&acc)[NI][NJ],
                                            int64_t row0, int64_t row1, int row_base,
                                            bool is_gate, int pair, int slot, int gcol, int64_t nt,
@@ -252,34 +255,44 @@ __device__ __forceinline__ void epi_swiglu(const GemmProblem& p, const f32x4 (&a
   const int frow = lane & 15;
   f32x4* ex_gate = s_ex + ((pair * 2 + 0) * NI * HJ) * 64;   // gate values for the up wave
   f32x4* ex_up = s_ex + ((pair * 2 + 1) * NI * HJ) * 64;     // up values for the gate wave
-  // (a bitwise select of two values read at constant indices: written as a
-  // branch, the compiler selected between the two accumulator addresses,
-  // which moved the accumulators to scratch memory)
-  const uint32_t keep_g = is_gate ? 0xffffffffu : 0u;
-  f32x4* ex_mine = is_gate ? ex_gate : ex_up;
+  // is_gate is wave-uniform: each kind of wave runs its own fully unrolled
+  // code, which indexes the accumulators with constants only (no selects)
+  if (is_gate) {
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < HJ; ++j) {
-      const u32x4 g_ = __builtin_bit_cast(u32x4, acc[i][HJ + j]);
-      const u32x4 u_ = __builtin_bit_cast(u32x4, acc[i][j]);
-      ex_mine[(i * HJ + j) * 64 + lane] = __builtin_bit_cast(f32x4, (g_ & keep_g) | (u_ & ~keep_g));
-    }
+      for (int j = 0; j < HJ; ++j) ex_gate[(i * HJ + j) * 64 + lane] = acc[i][HJ + j];
+  } else {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < HJ; ++j) ex_up[(i * HJ + j) * 64 + lane] = acc[i][j];
+  }
   __syncthreads();
   float av[NI][HJ][4];
   const int jo = is_gate ? 0 : HJ;
   const f32x4* ex_other = is_gate ? ex_up : ex_gate;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
+    if (is_gate) {
 #pragma unroll
-    for (int j = 0; j < HJ; ++j) {
-      const f32x4 other = ex_other[(i * HJ + j) * 64 + lane];
+      for (int j = 0; j < HJ; ++j) {
+        const f32x4 up = ex_other[(i * HJ + j) * 64 + lane];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        // scalar selects keep every acc index a constant
-        const float gt = is_gate ? acc[i][j][r] : other[r];
-        const float up = is_gate ? other[r] : acc[i][HJ + j][r];
-        av[i][j][r] = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * up;
+        for (int r = 0; r < 4; ++r) {
+          const float gt = acc[i][j][r];
+          av[i][j][r] = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * up[r];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < HJ; ++j) {
+        const f32x4 gate = ex_other[(i * HJ + j) * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gt = gate[r];
+          av[i][j][r] = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * acc[i][HJ + j][r];
+        }
       }
     }
 #pragma unroll
@@ -306,26 +319,44 @@ __device__ __forceinline__ void epi_swiglu(const GemmProblem& p, const f32x4 (&a
   }
   __syncthreads();
   const int ccol = gcol + jo * 16 + frow;
+  // codes from the rows' reciprocals; a wave with any unsure code encodes
+  // all of its values again from the IEEE quotients (rare)
+  bool unsure = false;
 #pragma unroll
   for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int r = 0; r < 4; r += 2) {   // rows lr, lr + 1: one packed conversion
       const int lr = row_base + i * 16 + (lane >> 4) * 4 + r;
-      const float sc0 = s_rmax[lr], sc1 = s_rmax[lr + 1];
+      const float rc0 = 1.0f / s_rmax[lr], rc1 = 1.0f / s_rmax[lr + 1];
 #pragma unroll
       for (int j = 0; j < HJ; ++j) {
-        const uint32_t c2 = e4m3_encode2(av[i][j][r] / sc0, av[i][j][r + 1] / sc1);
-        s_code[lr * 128 + ccol + j * 16] = static_cast<uint8_t>(c2);
-        s_code[(lr + 1) * 128 + ccol + j * 16] = static_cast<uint8_t>(c2 >> 8);
+        const uint32_t c2 = e4m3_encode2_recip(av[i][j][r], av[i][j][r + 1], rc0, rc1, unsure);
+        s_code[lr * CS + ccol + j * 16] = static_cast<uint8_t>(c2);
+        s_code[(lr + 1) * CS + ccol + j * 16] = static_cast<uint8_t>(c2 >> 8);
       }
     }
+  if (__builtin_amdgcn_ballot_w64(unsure) != 0) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const int lr = row_base + i * 16 + (lane >> 4) * 4 + r;
+        const float sc0 = s_rmax[lr], sc1 = s_rmax[lr + 1];
+#pragma unroll
+        for (int j = 0; j < HJ; ++j) {
+          const uint32_t c2 = e4m3_encode2(av[i][j][r] / sc0, av[i][j][r + 1] / sc1);
+          s_code[lr * CS + ccol + j * 16] = static_cast<uint8_t>(c2);
+          s_code[(lr + 1) * CS + ccol + j * 16] = static_cast<uint8_t>(c2 >> 8);
+        }
+      }
+  }
   __syncthreads();
   for (int idx = threadIdx.x; idx < ROWS * 8; idx += blockDim.x) {
     const int lr = idx >> 3, seg = idx & 7;
     const int64_t row = row0 + lr;
     if (row < row1)
       *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.c) + row * I + nt * 128 + seg * 16) =
-          *reinterpret_cast<const u32x4*>(&s_code[lr * 128 + seg * 16]);
+          *reinterpret_cast<const u32x4*>(&s_code[lr * CS + seg * 16]);
   }
 }
 
@@ -915,7 +946,7 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   } else {  // wn = 0 waves hold the 128 gate columns, wn = 1 the matching up columns
     // s_ex [4 pairs][2][4][4][64] f32x4 = 128 KB; the codes reuse its start
     // (the exchange is read before the barrier that precedes the codes)
-    epi_swiglu<4, 8, L2BM, 2>(p, acc, row0, row1, wm * 64, wn == 0, wm, wn, 0, nt,
+    epi_swiglu<4, 8, L2BM, 2, 144>(p, acc, row0, row1, wm * 64, wn == 0, wm, wn, 0, nt,
                               reinterpret_cast<f32x4*>(&s_stage[0][0]), &s_sa[0][0],
                               &s_stage[0][0]);
   }
