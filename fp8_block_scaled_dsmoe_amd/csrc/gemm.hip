@@ -689,7 +689,10 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
 #define DSMOE_WROW(lc) (w_row_base + (lc) + ((lc) >= 128 ? w_up_shift : 0))
 
   // Every wave copies 4 of the chunk's 32 A wave-loads and 4 of its 32 W
-  // wave-loads: wave-load jj covers tile rows 8jj .. 8jj+7 (lane -> row
+  // wave-loads (the A rows of wave w's copies, 32w .. 32w+31, lie in its own
+  // 64-row slice, so a wave whose slice has no row of the tile skips them, as
+  // it skips their scales, fragment reads and MFMAs): wave-load jj covers
+  // tile rows 8jj .. 8jj+7 (lane -> row
   // 8jj + lane/8, physical segment lane%8 holding logical segment
   // (lane%8) ^ swz_key(row); swz_key(row) is (lane/8) ^ (jj & 1) for these
   // rows).  A copies keep the gathered row of each load (32-bit) and form the
@@ -728,7 +731,7 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   do {                                                                                       \
     const int ch_ = min(static_cast<int>(blk) * C::SA_BLOCK + lane % C::SA_BLOCK,            \
                         static_cast<int>(kchunks) - 1);                                      \
-    _Pragma("unroll") for (int i = 0; i < CP; ++i) {                                         \
+    if (nsl > 0) _Pragma("unroll") for (int i = 0; i < CP; ++i) {                            \
       const uint32_t ld_ = __builtin_amdgcn_readfirstlane(                                   \
           sa_base + ((blk) & 1) * (L2BM * C::SA_BLOCK * 4) + (wave * CP + i) * 256);         \
       if constexpr (kA32)                                                                    \
@@ -742,6 +745,7 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
 #define DSMOE_ISSUE1(cc, st, i)                                                              \
   do {                                                                                       \
     if ((i) < CP) {                                                                          \
+      if (nsl == 0) break;  /* no row of the wave's slice: its A rows are never read */      \
       const int jj = wave * CP + (i);                                                        \
       if constexpr (kA32) {                                                                  \
         dma_16_buf(a_rsrc, static_cast<uint32_t>(arow[i]),                                   \
