@@ -86,8 +86,8 @@ def parse():
                     help="v3_prefill_backward: dtype of the weight gradients")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None,
-                    help="tokens of the batch the CPU oracle runs (default: 64 for v3_skew, whose tokens "
-                         "share few experts, else 14; about 10 s of oracle work either way)")
+                    help="tokens of the batch the CPU oracle runs (default: 128 for v3_skew, whose tokens "
+                         "share few experts, else 14; about 10-15 s of oracle work either way)")
     ap.add_argument("--balance-steps", type=int, default=1000,
                     help="layer workloads: routing-only bias updates for the imbalance trajectory (0: none)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -129,6 +129,13 @@ def measured_traffic(workload):
     read-request counters, writes from the write-request counters), or None."""
     t = gemm1_counters(workload)
     return None if t is None or "traffic_bytes_per_launch" not in t else int(t["traffic_bytes_per_launch"])
+
+
+def measured_traffic_algorithmic(workload):
+    """Algorithmic bytes of the gate/up launches the traffic counters were
+    taken on (their routing can differ from this run's), or None."""
+    t = gemm1_counters(workload)
+    return None if t is None else t.get("algorithmic_bytes_of_profiled_launches")
 
 
 def measured_mfma(workload):
@@ -812,6 +819,12 @@ def main():
     del dbg0
     log("load imbalance (max/mean): before " + f"{balance['before']['max_over_mean']:.3f}, after one update "
         f"{balance['after_one_update']['max_over_mean']:.3f}")
+    # (with no warm-up and two timed steps, the run's gate/up launches route
+    # exactly so: initial, updated, initial, updated -- the bias is reset
+    # above -- which sets a profiled run's traffic against those launches'
+    # own algorithmic bytes)
+    log(f"experts touched: {int(np.count_nonzero(counts_before))} with the initial bias, "
+        f"{int(np.count_nonzero(counts_after1))} after one update")
 
     for _ in range(args.warmup):
         step()
@@ -881,6 +894,7 @@ def main():
         "roofline": {"bound": g1_bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(cfg.name),
+                     "traffic_algorithmic_bytes": measured_traffic_algorithmic(cfg.name),
                      "mfma_busy_frac": measured_mfma(cfg.name),
                      "kernel": "gate/up grouped FP8 GEMM + SwiGLU + 1x128 requant (one launch)",
                      "algorithmic_bytes": int(g1_bytes), "algorithmic_flops": g1_flops,
@@ -899,7 +913,7 @@ def main():
         "load_balance": dict(balance, last_timed_step=imbalance(counts_last)),
     }
     if not args.no_cpu_baseline:
-        n_cpu = args.cpu_tokens if args.cpu_tokens is not None else (64 if cfg.zipf_s else 14)
+        n_cpu = args.cpu_tokens if args.cpu_tokens is not None else (128 if cfg.zipf_s else 14)
         result["cpu_baseline"] = cpu_baseline(cfg, n_cpu, torch, dsi)
     print(json.dumps(result), flush=True)
 
