@@ -618,13 +618,13 @@ __global__ __launch_bounds__(2 * BN) void gemm_lds_kernel(GemmProblem p, int64_t
 // (4 x 8 MFMA tiles, 128 accumulator registers).  A and W chunks (32 KB each)
 // come HBM -> LDS by DMA into two stages; per chunk a wave reads its 4 A
 // fragments once and streams its 8 W fragments, 0.75 KB of LDS per MFMA
-// (the 64 x 64 waves of the 128-row kernel read 1 KB).  The chunk's 32
-// MFMAs run as one sequence in which each step issues one MFMA and promotes
+// (the 64 x 64 waves of the 128-row kernel read 1 KB).  The MFMAs of all
+// chunks form one sequence in which each step issues one MFMA and promotes
 // the one issued two steps earlier, so LDS reads, MFMAs and promotions
-// overlap; partial sums rotate through a three-deep ring.  A wave whose 64
-// rows all lie past the tile's rows skips its reads, MFMAs and promotions
-// (finer, per-slice guards cost the schedule its registers: the
-// accumulators spilled).
+// overlap (see the main loop).  A wave whose 64 rows all lie past the tile's
+// rows skips its copies of A, its reads, MFMAs and promotions (finer,
+// per-slice guards cost the schedule its registers: the accumulators
+// spilled).
 constexpr int L2BM = 256;
 #ifndef DSMOE_LDS2
 #define DSMOE_LDS2 1
