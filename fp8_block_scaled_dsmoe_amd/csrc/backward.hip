@@ -309,8 +309,7 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const uint8_t* __restrict__ 
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          w[e] = static_cast<uint32_t>(f32_to_bf16(v[8 * q + 2 * e])) |
-                 (static_cast<uint32_t>(f32_to_bf16(v[8 * q + 2 * e + 1])) << 16);
+          w[e] = f32x2_to_bf16x2(v[8 * q + 2 * e], v[8 * q + 2 * e + 1]);
         dst[q] = w;
       }
     }

@@ -179,6 +179,18 @@ __device__ __forceinline__ void epi_rows(const GemmProblem& p, const f32x4 (&acc
   constexpr int PER = NCOL / 4;  // columns per lane
   const int lane = threadIdx.x & 63;
   const int64_t N = p.N;
+  const int lr = lane >> 2;
+  const int lc = (lane & 3) * PER;
+  // the row gates of all slices are loaded first: a load between the slices'
+  // stores would wait for those stores to complete (vmcnt counts both)
+  [[maybe_unused]] float gate[NI];
+  if constexpr (EPI == Epilogue::kGateStore) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int64_t row = row0 + row_base + i * 16 + lr;
+      gate[i] = row < row1 ? p.row_gate[row] : 0.0f;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
 #pragma unroll
@@ -188,8 +200,6 @@ __device__ __forceinline__ void epi_rows(const GemmProblem& p, const f32x4 (&acc
         scratch[((lane >> 4) * 4 + r) * S + j * 16 + (lane & 15)] = acc[i][j][r];
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
-    const int lr = lane >> 2;
-    const int lc = (lane & 3) * PER;
     const int64_t row = row0 + row_base + i * 16 + lr;
     float v[PER];
 #pragma unroll
@@ -199,9 +209,8 @@ __device__ __forceinline__ void epi_rows(const GemmProblem& p, const f32x4 (&acc
     if (row < row1) {
       const int64_t col = col0 + lc;
       if constexpr (EPI == Epilogue::kGateStore) {
-        const float gsc = p.row_gate[row];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) v[e] = v[e] * gsc;
+        for (int e = 0; e < PER; ++e) v[e] = v[e] * gate[i];
       }
       if (p.c_f32) {
         f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(p.c) + row * N + col);
@@ -214,8 +223,7 @@ __device__ __forceinline__ void epi_rows(const GemmProblem& p, const f32x4 (&acc
           u32x4 w;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            w[e] = static_cast<uint32_t>(f32_to_bf16(v[8 * q + 2 * e])) |
-                   (static_cast<uint32_t>(f32_to_bf16(v[8 * q + 2 * e + 1])) << 16);
+            w[e] = f32x2_to_bf16x2(v[8 * q + 2 * e], v[8 * q + 2 * e + 1]);
           dst[q] = w;
         }
       }
@@ -611,11 +619,188 @@ __global__ __launch_bounds__(2 * BN) void gemm_lds_kernel(GemmProblem p, int64_t
   }
 }
 
+// ---------------------------------------------------------------------------
+// Epilogues of the 256 x 256 kernel.  Its MFMAs take the weight fragment as
+// the first operand, so a lane holds one row and four adjacent columns of
+// each 16 x 16 tile, and its weight rows are staged in an order that makes
+// the two tiles of a fragment pair adjacent: for row slice i and pair pp,
+// lane l holds row row_base + 16 i + l % 16 and the 8 contiguous columns
+// 32 pp + 8 (l / 16) + [0, 8) of the wave's 128, acc[i][2pp] the first four
+// and acc[i][2pp + 1] the next four.  Both epilogues store straight from
+// registers, 16 (or 8) contiguous bytes per lane, with no LDS staging.
+// ---------------------------------------------------------------------------
+//   kStore      c[row][col] = acc
+//   kGateStore  c[row][col] = acc * row_gate[row]
+template <Epilogue EPI>
+__device__ __forceinline__ void epi_rows_lds2(const GemmProblem& p, const f32x4 (&acc)[4][8],
+                                              int64_t row0, int64_t row1, int row_base, int64_t col0) {
+  const int lane = threadIdx.x & 63;
+  const int64_t N = p.N;
+  const int64_t r_lane = row0 + row_base + (lane & 15);
+  const int64_t c_lane = col0 + 8 * (lane >> 4);
+  // the row gates of all slices are loaded before any store (a load issued
+  // after stores would wait for them: vmcnt counts both)
+  [[maybe_unused]] float gate[4];
+  if constexpr (EPI == Epilogue::kGateStore) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gate[i] = r_lane + 16 * i < row1 ? p.row_gate[r_lane + 16 * i] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = r_lane + 16 * i;
+    if (row >= row1) continue;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      f32x4 lo = acc[i][2 * pp], hi = acc[i][2 * pp + 1];
+      if constexpr (EPI == Epilogue::kGateStore) {
+        lo = lo * gate[i];
+        hi = hi * gate[i];
+      }
+      const int64_t off = row * N + c_lane + 32 * pp;
+      if (p.c_f32) {
+        f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(p.c) + off);
+        dst[0] = lo;
+        dst[1] = hi;
+      } else {
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.c) + off) =
+            u32x4{f32x2_to_bf16x2(lo[0], lo[1]), f32x2_to_bf16x2(lo[2], lo[3]),
+                  f32x2_to_bf16x2(hi[0], hi[1]), f32x2_to_bf16x2(hi[2], hi[3])};
+      }
+    }
+  }
+}
+
+// SwiGLU + 1x128 requantisation in the same layout.  The block tile holds
+// 128 gate columns (wn = 0 waves) and the matching 128 up columns (wn = 1
+// waves); the two waves of a row band (pair) use the same lane map.  The
+// gate wave finishes fragment pairs 0-1 (columns 0-63), the up wave pairs
+// 2-3, each receiving the other's half through LDS (s_ex, indexed by
+// (slice, fragment, lane): contiguous 16-byte runs).  a = silu(g) * u in
+// float32 (silu(g) = g * rcp(1 + exp(-g))); a row's amax is the lane's own
+// maximum, reduced over the 4 lanes that share the row (lanes 16 apart) and
+// over the two waves through s_rmax, where one thread per row turns it into
+// scale = amax / 448 (IEEE division) and stores it.  Codes are those of the
+// IEEE quotient a / scale: taken from a * (1 / scale) where a bracket proves
+// them equal (e4m3_encode2_recip), re-encoded from the quotient by any wave
+// with an unsure value.  A lane's 8 codes of a pair are one 8-byte store.
+//   s_ex:   [4 pairs][2][4 slices][4 fragments][64 lanes] f32x4 (128 KB)
+//   s_rmax: [2][256] f32
+__device__ __forceinline__ void epi_swiglu_lds2(const GemmProblem& p, const f32x4 (&acc)[4][8],
+                                                int64_t row0, int64_t row1, int row_base, bool is_gate,
+                                                int pair, int64_t nt, f32x4* s_ex, float* s_rmax) {
+  constexpr int ROWS = 256;
+  const int lane = threadIdx.x & 63;
+  const int frow = lane & 15;
+  f32x4* ex_gate = s_ex + ((pair * 2 + 0) * 16) * 64;   // gate values for the up wave
+  f32x4* ex_up = s_ex + ((pair * 2 + 1) * 16) * 64;     // up values for the gate wave
+  if (is_gate) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ex_gate[(i * 4 + j) * 64 + lane] = acc[i][4 + j];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ex_up[(i * 4 + j) * 64 + lane] = acc[i][j];
+  }
+  __syncthreads();
+  float av[4][4][4];   // [slice][fragment of the wave's half][column]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float m = 0.0f;
+    if (is_gate) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 up = ex_up[(i * 4 + j) * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gt = acc[i][j][r];
+          av[i][j][r] = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * up[r];
+          m = fmaxf(m, fabsf(av[i][j][r]));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 gate = ex_gate[(i * 4 + j) * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gt = gate[r];
+          av[i][j][r] = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * acc[i][4 + j][r];
+          m = fmaxf(m, fabsf(av[i][j][r]));
+        }
+      }
+    }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    if (lane < 16) s_rmax[(is_gate ? 0 : ROWS) + row_base + i * 16 + frow] = m;
+  }
+  __syncthreads();
+  const int64_t I = p.N / 2;
+  // one thread per row: the row's scale, stored and left in s_rmax[row]
+  for (int lr = threadIdx.x; lr < ROWS; lr += blockDim.x) {
+    const float amax = fmaxf(s_rmax[lr], s_rmax[ROWS + lr]);
+    const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+    s_rmax[lr] = sc;
+    const int64_t row = row0 + lr;
+    if (row < row1) p.c_scale[row * (I / BK) + nt] = sc;
+  }
+  __syncthreads();
+  // codes from the rows' reciprocals; a wave with any unsure code encodes
+  // all of its values again from the IEEE quotients (rare)
+  uint32_t code[4][2][2];   // [slice][local pair][word]
+  bool unsure = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float rc = 1.0f / s_rmax[row_base + i * 16 + frow];
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float* v = av[i][2 * pl + h];
+        const uint32_t c01 = e4m3_encode2_recip(v[0], v[1], rc, rc, unsure);
+        const uint32_t c23 = e4m3_encode2_recip(v[2], v[3], rc, rc, unsure);
+        code[i][pl][h] = (c01 & 0xFFFFu) | (c23 << 16);
+      }
+  }
+  if (__builtin_amdgcn_ballot_w64(unsure) != 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float sc = s_rmax[row_base + i * 16 + frow];
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float* v = av[i][2 * pl + h];
+          const uint32_t c01 = e4m3_encode2(v[0] / sc, v[1] / sc);
+          const uint32_t c23 = e4m3_encode2(v[2] / sc, v[3] / sc);
+          code[i][pl][h] = (c01 & 0xFFFFu) | (c23 << 16);
+        }
+    }
+  }
+  const int pbase = is_gate ? 0 : 2;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row0 + row_base + i * 16 + frow;
+    if (row >= row1) continue;
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl) {
+      uint8_t* dst = static_cast<uint8_t*>(p.c) + row * I + nt * 128 + 32 * (pbase + pl) + 8 * (lane >> 4);
+      *reinterpret_cast<uint2*>(dst) = uint2{code[i][pl][0], code[i][pl][1]};
+    }
+  }
+}
+
 // ===========================================================================
 // gemm_lds2_kernel: 256 x 256 tiles for groups of many rows (MFMA-bound)
 // ===========================================================================
 // Eight waves as 4 (rows) x 2 (columns), each owning 64 rows x 128 columns
-// (4 x 8 MFMA tiles, 128 accumulator registers).  A and W chunks (32 KB each)
+// (4 x 8 MFMA tiles, 128 accumulator registers).  The MFMAs take the weight
+// fragment as their first operand, so a lane's four results of a tile lie in
+// one row: one row scale per lane and slice promotes them, and the epilogues
+// store a lane's adjacent columns straight from registers (the weight rows
+// are staged in the order that makes them adjacent).  A and W chunks (32 KB each)
 // come HBM -> LDS by DMA into two stages; per chunk a wave reads its 4 A
 // fragments once and streams its 8 W fragments, 0.75 KB of LDS per MFMA
 // (the 64 x 64 waves of the 128-row kernel read 1 KB).  The MFMAs of all
@@ -715,10 +900,17 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   }
   const i32x4_rsrc a_rsrc = buffer_rsrc(p.a);
   const i32x4_rsrc w_rsrc = buffer_rsrc(wbase);
+  // W rows are staged in the order that the epilogues' layout needs: LDS
+  // row 128 h + 16 j + m (h: column half, j: fragment, m = 4 q + r: the
+  // fragment's row) holds tile column 128 h + 32 (j / 2) + 8 q + 4 (j % 2) + r.
+  // For the 8 LDS rows 8 jj + t of W wave-load jj that is a wave-uniform
+  // column w_col(jj) plus 8 (t / 4) + t % 4.
   uint32_t w_voff[2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
-    w_voff[par] = static_cast<uint32_t>((lane >> 3) * K + (((lane & 7) ^ (lane >> 3) ^ par) << 4));
+  for (int par = 0; par < 2; ++par) {
+    const int t = lane >> 3;
+    w_voff[par] = static_cast<uint32_t>((8 * (t >> 2) + (t & 3)) * K + (((lane & 7) ^ t ^ par) << 4));
+  }
   const uint32_t st_base = lds_addr(&s_stage[0][0]);
   const uint32_t sa_base = lds_addr(&s_sa[0][0]);
   const i32x4_rsrc sa_rsrc = buffer_rsrc(p.a_scale);
@@ -760,7 +952,9 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
       }                                                                                      \
     } else {                                                                                 \
       const int jj = wave * CP + (i) - CP;                                                   \
-      const int64_t wr0 = w_row_base + jj * 8 + (jj * 8 >= 128 ? w_up_shift : 0);            \
+      const int jf_ = (jj >> 1) & 7;                                                         \
+      const int wc_ = 128 * (jj >> 4) + 32 * (jf_ >> 1) + 16 * (jj & 1) + 4 * (jf_ & 1);      \
+      const int64_t wr0 = w_row_base + wc_ + (wc_ >= 128 ? w_up_shift : 0);                  \
       dma_16_buf(w_rsrc, w_voff[(i) & 1],                                                    \
                  __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(wr0 * K + (cc) * BK)),  \
                  __builtin_amdgcn_readfirstlane(st_base + (st) * C::STAGE_BYTES + L2BM * BK + jj * 1024)); \
@@ -810,8 +1004,8 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   // its operands in registers instead of with every wave reading LDS at once.
   i32x8 fa[4], bf[2];
   f32x4 part[4];
-  float scl[4][4];
-  f32x4 s4n[4];
+  float scl[4];   // per row slice: the lane's row scale times the weight block's
+  float s4n[4];
   float swn;
   const uint8_t* st0 = &s_stage[0][0];
 #define DSMOE_RD_A(i_, stp)                                                                    \
@@ -826,26 +1020,25 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
     bf[(jj) & 1] = cat8(*reinterpret_cast<const u32x4*>((stp) + L2BM * BK + swz(r_, fseg)),   \
                         *reinterpret_cast<const u32x4*>((stp) + L2BM * BK + swz(r_, fseg + 1))); \
   } while (0)
-  // row scales of chunk cc for row slice i_ (4 rows per lane)
+  // the row scale of chunk cc for row slice i_ (one row per lane)
 #define DSMOE_RD_S(i_, cc)                                                                     \
   do {                                                                                         \
-    const float* sp_ = &s_sa[((cc) / C::SA_BLOCK) & 1][(wm * 64 + (i_) * 16 + (lane >> 4) * 4) * C::SA_BLOCK + \
-                                                        (cc) % C::SA_BLOCK];                   \
-    _Pragma("unroll") for (int rr = 0; rr < 4; ++rr) s4n[i_][rr] = sp_[rr * C::SA_BLOCK];      \
+    s4n[i_] = s_sa[((cc) / C::SA_BLOCK) & 1][(wm * 64 + (i_) * 16 + frow) * C::SA_BLOCK +     \
+                                             (cc) % C::SA_BLOCK];                              \
   } while (0)
 #define DSMOE_SCL(i_)                                                  \
   do {                                                                 \
-    _Pragma("unroll") for (int rr = 0; rr < 4; ++rr) scl[i_][rr] = s4n[i_][rr] * swn; \
+    scl[i_] = s4n[i_] * swn;                                           \
   } while (0)
   // one step: MFMA k, then the promotion of MFMA k-2 (ring slot (k-2) & 3)
 #define DSMOE_STEP(k, stp)                                                                     \
   do {                                                                                         \
     const int j_ = (k) >> 2, i_ = (k) & 3;                                                     \
     if (i_ == 0 && j_ + 1 < 8) DSMOE_RD_B(j_ + 1, stp);                                        \
-    part[(k) & 3] = mfma_chunk(fa[i_], bf[j_ & 1]);                                            \
+    part[(k) & 3] = mfma_chunk(bf[j_ & 1], fa[i_]);                                            \
     const int kp_ = ((k) + 30) & 31, jp_ = kp_ >> 2, ip_ = kp_ & 3;                            \
     _Pragma("unroll") for (int rr = 0; rr < 4; ++rr)                                           \
-      acc[ip_][jp_][rr] = __builtin_fmaf(part[kp_ & 3][rr], scl[ip_][rr], acc[ip_][jp_][rr]); \
+      acc[ip_][jp_][rr] = __builtin_fmaf(part[kp_ & 3][rr], scl[ip_], acc[ip_][jp_][rr]);     \
   } while (0)
   // per step: the MFMA, then its LDS reads, then its VALU work (a step
   // has at most 6 reads and 8 VALU instructions)
@@ -858,8 +1051,7 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   // chunk 0's operands; the promotions of steps 0 and 1 (the previous
   // chunk's last MFMAs, of which there are none) add 0 * 0
   part[2] = part[3] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) scl[2][rr] = scl[3][rr] = 0.f;
+  scl[2] = scl[3] = 0.f;
   if (nsl > 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -928,8 +1120,8 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   if (nsl > 0) {   // the last chunk's MFMAs 30 and 31
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      acc[2][7][rr] = __builtin_fmaf(part[2][rr], scl[2][rr], acc[2][7][rr]);
-      acc[3][7][rr] = __builtin_fmaf(part[3][rr], scl[3][rr], acc[3][7][rr]);
+      acc[2][7][rr] = __builtin_fmaf(part[2][rr], scl[2], acc[2][7][rr]);
+      acc[3][7][rr] = __builtin_fmaf(part[3][rr], scl[3], acc[3][7][rr]);
     }
   }
 #undef DSMOE_RD_A
@@ -941,18 +1133,14 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
 #undef DSMOE_ISSUE
 #undef DSMOE_ISSUE1
 #undef DSMOE_ISSUE_SA
-  __syncthreads();  // all waves are done with the stages (the epilogues reuse them)
-
   if constexpr (EPI != Epilogue::kSwiGLUQuant) {
-    static_assert(C::NW * epi_rows_scratch_floats<8>() * 4 <= sizeof(s_stage), "epilogue scratch fits the stages");
-    epi_rows<4, 8, EPI>(p, acc, row0, row1, wm * 64, nt * BN + wn * 128,
-                        reinterpret_cast<float*>(&s_stage[0][0]) + wave * epi_rows_scratch_floats<8>());
+    epi_rows_lds2<EPI>(p, acc, row0, row1, wm * 64, nt * BN + wn * 128);
   } else {  // wn = 0 waves hold the 128 gate columns, wn = 1 the matching up columns
-    // s_ex [4 pairs][2][4][4][64] f32x4 = 128 KB; the codes reuse its start
-    // (the exchange is read before the barrier that precedes the codes)
-    epi_swiglu<4, 8, L2BM, 2, 144>(p, acc, row0, row1, wm * 64, wn == 0, wm, wn, 0, nt,
-                              reinterpret_cast<f32x4*>(&s_stage[0][0]), &s_sa[0][0],
-                              &s_stage[0][0]);
+    __syncthreads();  // all waves are done with the stages (the exchange reuses them)
+    static_assert(4 * 2 * 16 * 64 * sizeof(f32x4) <= sizeof(s_stage) && 2 * L2BM <= L2BM * C::SA_BLOCK,
+                  "the exchange fits the stages and the row maxima the scale blocks");
+    epi_swiglu_lds2(p, acc, row0, row1, wm * 64, wn == 0, wm, nt, reinterpret_cast<f32x4*>(&s_stage[0][0]),
+                    &s_sa[0][0]);
   }
 }
 
@@ -1452,8 +1640,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o
     u32x4 w;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      w[e] = static_cast<uint32_t>(f32_to_bf16(v[2 * e])) |
-             (static_cast<uint32_t>(f32_to_bf16(v[2 * e + 1])) << 16);
+      w[e] = f32x2_to_bf16x2(v[2 * e], v[2 * e + 1]);
     *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + t * H + c0) = w;
   }
 }

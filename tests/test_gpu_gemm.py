@@ -48,6 +48,55 @@ def test_golden_two_chunk(golden):
         assert np.all(ch[0, 1:] == 0)
 
 
+# float32 bit patterns (positive) whose bf16 rounding is a corner case:
+# ties to even either way, one ulp off a tie, subnormals (ties, the smallest,
+# the largest, rounding up to the smallest normal), and the top of the range
+# (a tie that rounds to infinity, values just below and above it)
+_BF16_CORNERS = [0x3F808000, 0x3F818000, 0x3F807FFF, 0x3F808001, 0x3F800000, 0x3FFFFFFF,
+                 0x00008000, 0x00018000, 0x00000001, 0x0000C000, 0x007FFFFF, 0x00808000,
+                 0x7F7F7FFF, 0x7F7F8000, 0x7F7FFFFF, 0x7F7E8000, 0x0B7F8000, 0x34818000]
+
+
+# (M, N): the weight-streaming kernel, the 128-column LDS kernel, the 256 x 256 kernel
+@pytest.mark.parametrize("M,N", [(40, 256), (300, 128), (600, 256)])
+def test_bf16_output_rounding(M, N):
+    """bf16 outputs are the float32 results rounded to nearest, ties to even,
+    subnormals kept.  Every output is exact in float32: row r holds one
+    non-zero product, (+-1) x 1 at column 0, so c[r][n] = +-sa[r][0]; the row
+    scales are the corner patterns above and random positive floats.  The
+    float32 output must equal +-sa exactly and the bf16 output torch's CPU
+    rounding of it, bit for bit."""
+    d = _dsmoe()
+    r = np.random.default_rng(M + N)
+    K = 256
+    bits = r.integers(0x00000001, 0x7F800000, size=M, dtype=np.int64).astype(np.uint32)
+    bits[:len(_BF16_CORNERS)] = _BF16_CORNERS
+    vals = bits.view(np.float32)
+    neg = r.random(M) < 0.5
+    qa = np.zeros((M, K), np.uint8)
+    qa[:, 0] = np.where(neg, 0xB8, 0x38)            # -1.0 / +1.0
+    sa = np.ones((M, K // 128), np.float32)
+    sa[:, 0] = vals
+    qw = np.zeros((N, K), np.uint8)
+    qw[:, 0] = 0x38
+    sw = np.ones((N // 128, K // 128), np.float32)
+    want32 = np.where(neg, -vals, vals).astype(np.float32)
+    want16 = torch.from_numpy(want32).to(torch.bfloat16).view(torch.int16).numpy()
+    offs = dev(np.array([0, M], np.int32))
+    banner(f"gemm bf16 output rounding M={M} N={N}")
+    c32 = d.fp8_grouped_gemm(dev(qa), dev(sa), offs, dev(qw[None]), dev(sw[None]), out_dtype=torch.float32)
+    c16 = d.fp8_grouped_gemm(dev(qa), dev(sa), offs, dev(qw[None]), dev(sw[None]), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    g32 = c32.cpu().numpy()
+    g16 = c16.view(torch.int16).cpu().numpy()
+    assert np.array_equal(g32.view(np.uint32), np.repeat(want32.view(np.uint32)[:, None], N, axis=1)), \
+        "float32 output differs from the exact value"
+    bad = g16 != want16[:, None]
+    assert not bad.any(), f"{int(bad.sum())} bf16 outputs differ from round-to-nearest-even, e.g. " + \
+        ", ".join(f"{int(want32.view(np.uint32)[i]):#010x} -> {int(g16[i, j]) & 0xFFFF:#06x} "
+                  f"(want {int(want16[i]) & 0xFFFF:#06x})" for i, j in zip(*np.nonzero(bad)) if True)[:400]
+
+
 # (700, 256, 128) and (513, 768, 384): the 256 x 256 kernel with one and
 # three K chunks (its stage ring and cross-chunk pipeline at their shortest)
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (300, 384, 640), (129, 256, 1024), (1000, 512, 256),
