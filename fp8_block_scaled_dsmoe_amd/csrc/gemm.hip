@@ -30,6 +30,8 @@
 // device: every block derives its (group, row tile) from offsets[].  Logical
 // tile order is remapped so that consecutive tiles land on the same XCD
 // (blocks are dispatched round-robin over the 8 XCDs) and share its L2.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -75,6 +77,35 @@ __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
 // row1, column tile}; returns false past the end.
 constexpr int64_t kRowBand = 4;
 
+// Inclusive prefix sum of a 64-bit value over the 64 lanes of a wave: within
+// each row of 16 lanes by DPP shifts (row_shr 1, 2, 4, 8; a lane with no
+// source lane adds 0), then the totals of the lower rows, read from lanes 15,
+// 31 and 47.  (A shuffle per step through the LDS crossbar, two for 64 bits,
+// took most of the tile decode's time.)
+__device__ __forceinline__ int64_t wave_inclusive_scan64(int64_t v, int lane) {
+  auto shr = [](int64_t x, auto ctrl) {
+    const uint64_t u = static_cast<uint64_t>(x);
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u)), decltype(ctrl)::value, 0xF, 0xF, false));
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u >> 32)), decltype(ctrl)::value, 0xF, 0xF, false));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+  };
+  v += shr(v, std::integral_constant<int, 0x111>{});   // row_shr:1
+  v += shr(v, std::integral_constant<int, 0x112>{});   // row_shr:2
+  v += shr(v, std::integral_constant<int, 0x114>{});   // row_shr:4
+  v += shr(v, std::integral_constant<int, 0x118>{});   // row_shr:8
+  auto lane64 = [&](int src) {
+    const uint64_t u = static_cast<uint64_t>(v);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u)), src));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u >> 32)), src));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+  };
+  const int64_t t0 = lane64(15), t1 = lane64(31), t2 = lane64(47);
+  const int row = lane >> 4;
+  return v + (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
+}
+
 template <int THREADS, int TILE_M>
 __device__ bool decode_tile(const int32_t* __restrict__ offsets, int32_t G, int64_t logical,
                             int64_t n_tiles, int64_t* s_scan, int64_t* s_out) {
@@ -92,12 +123,7 @@ __device__ bool decode_tile(const int32_t* __restrict__ offsets, int32_t G, int6
     }
     // inclusive scan of the group's tile count (row tiles x column tiles)
     const int64_t mine = static_cast<int64_t>(cnt) * n_tiles;
-    int64_t v = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int64_t u = __shfl_up(v, o, 64);
-      if (lane >= o) v += u;
-    }
+    const int64_t v = wave_inclusive_scan64(mine, lane);
     if (lane == 63) s_scan[wave] = v;
     __syncthreads();
     int64_t wbase = 0, total = 0;
