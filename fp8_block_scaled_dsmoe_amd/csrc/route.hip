@@ -132,6 +132,118 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
     }
 }
 
+// Wide variant for E a multiple of 256 and at least 128 tokens: block tile
+// 128 tokens x 256 experts, eight waves as 2 (tokens) x 4 (experts), each
+// 64 x 64 (4 x 4 MFMA tiles).  A block reads its x rows once for 256
+// experts, where the 64 x 64 tiles read them once per 64, and keeps two K
+// steps of loads in flight in registers: the step's data goes to LDS at the
+// end of the step before, and the step after next is loaded at its start.
+// (At 32768 tokens the 64 x 64 kernel, with one step of loads in flight,
+// waited on them; 0.30 ms for 120 GFLOP.)  Same MFMA, same order of FP32
+// accumulation over K and the same splits-and-reduce scheme as above.
+constexpr int WRT = 128, WRE = 256;
+constexpr int WSEGS = (WRT + WRE) * (RK * 2 / 16) / 512;   // 16-byte segments per thread and step
+
+__global__ __launch_bounds__(512) void router_logits_wide_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ wr,
+                                                                 int64_t T, int64_t H, int32_t E,
+                                                                 int64_t k_len, float* __restrict__ z) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][(WRT + WRE) * 128];   // x rows, then W rows
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * WRT;
+  const int e0 = blockIdx.y * WRE;
+  const int64_t k_begin = static_cast<int64_t>(blockIdx.z) * k_len;
+  z += static_cast<int64_t>(blockIdx.z) * T * E;
+
+  // segment i of this thread: tile row idx / 8 (x rows 0..127, W rows
+  // 128..383), 16-byte segment idx % 8 of the step's 128 bytes
+  const uint16_t* src[WSEGS];
+  int dst[WSEGS];
+#pragma unroll
+  for (int i = 0; i < WSEGS; ++i) {
+    const int idx = tid + 512 * i;
+    const int row = idx >> 3, seg = idx & 7;
+    if (row < WRT) {
+      const int64_t tr = min<int64_t>(t0 + row, T - 1);
+      src[i] = x + tr * H + k_begin + seg * 8;
+    } else {
+      src[i] = wr + static_cast<int64_t>(e0 + row - WRT) * H + k_begin + seg * 8;
+    }
+    dst[i] = swz(row, seg);
+  }
+  u32x4 ld[2][WSEGS];
+#define DSMOE_WLOAD(set, k0)                                                                   \
+  do {                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < WSEGS; ++i)                                          \
+      ld[set][i] = *reinterpret_cast<const u32x4*>(src[i] + (k0));                             \
+  } while (0)
+#define DSMOE_WSTORE(set, bb)                                                                  \
+  do {                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < WSEGS; ++i)                                          \
+      *reinterpret_cast<u32x4*>(&lds[(bb)][dst[i]]) = ld[set][i];                              \
+  } while (0)
+
+  const int wm = wave >> 2, wn = wave & 3;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // one K step on buffer bb: two MFMA K slices of 32
+#define DSMOE_WCOMPUTE(bb)                                                                     \
+  do {                                                                                         \
+    _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                         \
+      const int seg = ks * 4 + (lane >> 4);                                                    \
+      bf16x8 af[4], bfr[4];                                                                    \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                          \
+        af[i] = *reinterpret_cast<const bf16x8*>(&lds[(bb)][swz(wm * 64 + i * 16 + (lane & 15), seg)]); \
+        bfr[i] = *reinterpret_cast<const bf16x8*>(                                             \
+            &lds[(bb)][swz(WRT + wn * 64 + i * 16 + (lane & 15), seg)]);                        \
+      }                                                                                        \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                            \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0); \
+    }                                                                                          \
+  } while (0)
+
+  const int64_t steps = k_len / RK;
+  DSMOE_WLOAD(0, 0);
+  if (steps > 1) DSMOE_WLOAD(1, RK);
+  DSMOE_WSTORE(0, 0);
+  __syncthreads();
+  // step s uses buffer s & 1 and register set s & 1 (the loop is unrolled by
+  // two so that the sets are indexed with constants)
+  for (int64_t st = 0; st < steps; st += 2) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t s_ = st + b;
+      if (s_ < steps) {
+        if (s_ + 2 < steps) DSMOE_WLOAD(b, (s_ + 2) * RK);   // set b's step is in LDS already
+        DSMOE_WCOMPUTE(b);
+        if (s_ + 1 < steps) DSMOE_WSTORE(b ^ 1, b ^ 1);      // buffer b^1 was read in step s-1
+        __syncthreads();
+      }
+    }
+  }
+#undef DSMOE_WLOAD
+#undef DSMOE_WSTORE
+#undef DSMOE_WCOMPUTE
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + wn * 64 + j * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+        if (t < T) z[t * E + e] = acc[i][j][r];
+      }
+    }
+}
+
 // z[t][e] = sum over splits s = 0, 1, ... of part[s][t][e], in that order;
 // 4 values per thread.  The splits are loaded 8 at a time before they are
 // added (in the same order): one load per iteration waited for each load in
@@ -495,13 +607,18 @@ __global__ void update_bias_kernel(float* __restrict__ bias, const int32_t* __re
 
 }  // namespace
 
+bool router_wide(int64_t T, int32_t E) { return E % WRE == 0 && T >= WRT; }
+
 int router_splits(int64_t T, int64_t H, int32_t E) {
-  // enough blocks to cover the device four times (about 1024; 512 was 15%
-  // slower at 4096 tokens, 2048 no faster), each split at least 256 columns
-  // long, and T * E a multiple of 4 for the reduction
-  const int64_t base = ((T + RT - 1) / RT) * ((E + RE - 1) / RE);
-  if (base <= 0 || base >= 1024 || (T * E) % 4 != 0) return 1;
-  int64_t want = (1024 + base - 1) / base;
+  // 64 x 64 tiles: enough blocks to cover the device four times (about 1024;
+  // 512 was 15% slower at 4096 tokens, 2048 no faster).  The wide tiles (one
+  // block per CU: 96 KB of LDS) aim at 256 blocks.  Each split is at least
+  // 256 columns long, and T * E a multiple of 4 for the reduction.
+  const bool wide = router_wide(T, E);
+  const int64_t base = wide ? ((T + WRT - 1) / WRT) * (E / WRE) : ((T + RT - 1) / RT) * ((E + RE - 1) / RE);
+  const int64_t target = wide ? 256 : 1024;
+  if (base <= 0 || base >= target || (T * E) % 4 != 0) return 1;
+  int64_t want = (target + base - 1) / base;
   const int64_t steps = H / RK;
   int best = 1;
   for (int64_t sp = 2; sp <= want && sp * 4 <= steps; ++sp)
@@ -518,9 +635,15 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, int64_t T
                                 int32_t E, float* logits, float* partial, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int sp = router_splits(T, H, E);
-  const dim3 grid(static_cast<unsigned>((T + RT - 1) / RT), static_cast<unsigned>((E + RE - 1) / RE),
-                  static_cast<unsigned>(sp));
-  router_logits_kernel<<<grid, 256, 0, s>>>(x, wr, T, H, E, H / sp, sp > 1 ? partial : logits);
+  if (router_wide(T, E)) {
+    const dim3 grid(static_cast<unsigned>((T + WRT - 1) / WRT), static_cast<unsigned>(E / WRE),
+                    static_cast<unsigned>(sp));
+    router_logits_wide_kernel<<<grid, 512, 0, s>>>(x, wr, T, H, E, H / sp, sp > 1 ? partial : logits);
+  } else {
+    const dim3 grid(static_cast<unsigned>((T + RT - 1) / RT), static_cast<unsigned>((E + RE - 1) / RE),
+                    static_cast<unsigned>(sp));
+    router_logits_kernel<<<grid, 256, 0, s>>>(x, wr, T, H, E, H / sp, sp > 1 ? partial : logits);
+  }
   if (sp > 1) {
     const int64_t n = T * E;
     router_reduce_kernel<<<static_cast<unsigned>((n / 4 + 255) / 256), 256, 0, s>>>(partial, sp, n, logits);

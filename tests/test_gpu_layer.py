@@ -152,6 +152,11 @@ def test_tiny_layer_deterministic():
     # 16- and 32-row weight-streaming tiles
     LayerConfig("few7", T=7, H=512, E=16, G=4, Mg=2, K=4, I=256, router_std=0.05),
     LayerConfig("few20", T=20, H=512, E=16, G=4, Mg=2, K=4, I=256, router_std=0.05),
+    # 256 experts or a multiple: the router logits take the 128 x 256 tiles,
+    # here with H split in two (ragged last token tile) and in four (two
+    # expert tiles)
+    LayerConfig("e256", T=300, H=512, E=256, G=8, Mg=4, K=8, I=128, router_std=0.02, bias_range=0.01),
+    LayerConfig("e512", T=128, H=1024, E=512, G=8, Mg=4, K=8, I=128, router_std=0.02, bias_range=0.01),
 ], ids=lambda c: c.name)
 def test_layer_shapes(cfg):
     _layer_case(cfg, torch.float32)
