@@ -653,7 +653,8 @@ __global__ __launch_bounds__(2 * BN) void gemm_lds_kernel(GemmProblem p, int64_t
 // lane l holds row row_base + 16 i + l % 16 and the 8 contiguous columns
 // 32 pp + 8 (l / 16) + [0, 8) of the wave's 128, acc[i][2pp] the first four
 // and acc[i][2pp + 1] the next four.  Both epilogues store straight from
-// registers, 16 (or 8) contiguous bytes per lane, with no LDS staging.
+// registers, 16 (or 8) contiguous bytes per lane, with no LDS staging.  (The
+// SwiGLU epilogue's tile has its own column order: see epi_swiglu_pairs.)
 // ---------------------------------------------------------------------------
 //   kStore      c[row][col] = acc
 //   kGateStore  c[row][col] = acc * row_gate[row]
@@ -696,71 +697,40 @@ __device__ __forceinline__ void epi_rows_lds2(const GemmProblem& p, const f32x4 
   }
 }
 
-// SwiGLU + 1x128 requantisation in the same layout.  The block tile holds
-// 128 gate columns (wn = 0 waves) and the matching 128 up columns (wn = 1
-// waves); the two waves of a row band (pair) use the same lane map.  The
-// gate wave finishes fragment pairs 0-1 (columns 0-63), the up wave pairs
-// 2-3, each receiving the other's half through LDS (s_ex, indexed by
-// (slice, fragment, lane): contiguous 16-byte runs).  a = silu(g) * u in
-// float32 (silu(g) = g * rcp(1 + exp(-g))); a row's amax is the lane's own
-// maximum, reduced over the 4 lanes that share the row (lanes 16 apart) and
-// over the two waves through s_rmax, where one thread per row turns it into
-// scale = amax / 448 (IEEE division) and stores it.  Codes are those of the
-// IEEE quotient a / scale: taken from a * (1 / scale) where a bracket proves
-// them equal (e4m3_encode2_recip), re-encoded from the quotient by any wave
-// with an unsure value.  A lane's 8 codes of a pair are one 8-byte store.
-//   s_ex:   [4 pairs][2][4 slices][4 fragments][64 lanes] f32x4 (128 KB)
+// SwiGLU + 1x128 requantisation for the 256 x 256 kernel with gate and up
+// columns paired inside each wave: wave (wm, wn) holds output columns
+// [64 wn, 64 wn + 64) of the tile's 128, their gate values in fragments 0-3
+// and the matching up values in fragments 4-7 (same lane, same positions),
+// so a = silu(g) * u is formed in registers without any exchange.  A row's
+// amax: the lane's own 16 values, then the 4 lanes that share the row
+// (lanes 16 apart), then the two waves of the row band through s_rmax,
+// where one thread per row forms scale = amax / 448 (IEEE division) and
+// stores it.  Codes are those of the IEEE quotient a / scale: taken from
+// a * (1 / scale) where a bracket proves them equal (e4m3_encode2_recip),
+// re-encoded from the quotient by any wave with an unsure value.  A lane's 8
+// codes of a fragment pair leave as one 8-byte store.
 //   s_rmax: [2][256] f32
-__device__ __forceinline__ void epi_swiglu_lds2(const GemmProblem& p, const f32x4 (&acc)[4][8],
-                                                int64_t row0, int64_t row1, int row_base, bool is_gate,
-                                                int pair, int64_t nt, f32x4* s_ex, float* s_rmax) {
+__device__ __forceinline__ void epi_swiglu_pairs(const GemmProblem& p, const f32x4 (&acc)[4][8],
+                                                 int64_t row0, int64_t row1, int row_base, int wn,
+                                                 int64_t nt, float* s_rmax) {
   constexpr int ROWS = 256;
   const int lane = threadIdx.x & 63;
   const int frow = lane & 15;
-  f32x4* ex_gate = s_ex + ((pair * 2 + 0) * 16) * 64;   // gate values for the up wave
-  f32x4* ex_up = s_ex + ((pair * 2 + 1) * 16) * 64;     // up values for the gate wave
-  if (is_gate) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ex_gate[(i * 4 + j) * 64 + lane] = acc[i][4 + j];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ex_up[(i * 4 + j) * 64 + lane] = acc[i][j];
-  }
-  __syncthreads();
-  float av[4][4][4];   // [slice][fragment of the wave's half][column]
+  float av[4][4][4];   // [slice][gate fragment][column]
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float m = 0.0f;
-    if (is_gate) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 up = ex_up[(i * 4 + j) * 64 + lane];
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float gt = acc[i][j][r];
-          av[i][j][r] = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * up[r];
-          m = fmaxf(m, fabsf(av[i][j][r]));
-        }
+      for (int r = 0; r < 4; ++r) {
+        const float gt = acc[i][j][r];
+        av[i][j][r] = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * acc[i][4 + j][r];
+        m = fmaxf(m, fabsf(av[i][j][r]));
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 gate = ex_gate[(i * 4 + j) * 64 + lane];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float gt = gate[r];
-          av[i][j][r] = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * acc[i][4 + j][r];
-          m = fmaxf(m, fabsf(av[i][j][r]));
-        }
-      }
-    }
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
-    if (lane < 16) s_rmax[(is_gate ? 0 : ROWS) + row_base + i * 16 + frow] = m;
+    if (lane < 16) s_rmax[wn * ROWS + row_base + i * 16 + frow] = m;
   }
   __syncthreads();
   const int64_t I = p.N / 2;
@@ -773,9 +743,7 @@ __device__ __forceinline__ void epi_swiglu_lds2(const GemmProblem& p, const f32x
     if (row < row1) p.c_scale[row * (I / BK) + nt] = sc;
   }
   __syncthreads();
-  // codes from the rows' reciprocals; a wave with any unsure code encodes
-  // all of its values again from the IEEE quotients (rare)
-  uint32_t code[4][2][2];   // [slice][local pair][word]
+  uint32_t code[4][2][2];   // [slice][fragment pair][word]
   bool unsure = false;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -805,14 +773,13 @@ __device__ __forceinline__ void epi_swiglu_lds2(const GemmProblem& p, const f32x
         }
     }
   }
-  const int pbase = is_gate ? 0 : 2;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t row = row0 + row_base + i * 16 + frow;
     if (row >= row1) continue;
 #pragma unroll
     for (int pl = 0; pl < 2; ++pl) {
-      uint8_t* dst = static_cast<uint8_t*>(p.c) + row * I + nt * 128 + 32 * (pbase + pl) + 8 * (lane >> 4);
+      uint8_t* dst = static_cast<uint8_t*>(p.c) + row * I + nt * 128 + 64 * wn + 32 * pl + 8 * (lane >> 4);
       *reinterpret_cast<uint2*>(dst) = uint2{code[i][pl][0], code[i][pl][1]};
     }
   }
@@ -822,7 +789,8 @@ __device__ __forceinline__ void epi_swiglu_lds2(const GemmProblem& p, const f32x
 // gemm_lds2_kernel: 256 x 256 tiles for groups of many rows (MFMA-bound)
 // ===========================================================================
 // Eight waves as 4 (rows) x 2 (columns), each owning 64 rows x 128 columns
-// (4 x 8 MFMA tiles, 128 accumulator registers).  The MFMAs take the weight
+// (4 x 8 MFMA tiles, 128 accumulator registers; for SwiGLU, 64 gate and the
+// matching 64 up columns).  The MFMAs take the weight
 // fragment as their first operand, so a lane's four results of a tile lie in
 // one row: one row scale per lane and slice promotes them, and the epilogues
 // store a lane's adjacent columns straight from registers (the weight rows
@@ -896,6 +864,9 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   const uint8_t* wbase = last ? p.w_last : p.w + static_cast<int64_t>(g) * N * K;
   const float* wsbase = last ? p.w_scale_last : p.w_scale + static_cast<int64_t>(g) * (N / BK) * kchunks;
   const int64_t w_row_base = (EPI == Epilogue::kSwiGLUQuant) ? nt * 128 : nt * BN;
+  // SwiGLU: each wave holds 64 gate columns (fragments 0-3) and the matching
+  // 64 up columns (fragments 4-7); see the W staging order below
+  constexpr bool kPair = EPI == Epilogue::kSwiGLUQuant;
   const int64_t w_up_shift = (EPI == Epilogue::kSwiGLUQuant) ? N / 2 - 128 : 0;
 #define DSMOE_WROW(lc) (w_row_base + (lc) + ((lc) >= 128 ? w_up_shift : 0))
 
@@ -927,10 +898,13 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   const i32x4_rsrc a_rsrc = buffer_rsrc(p.a);
   const i32x4_rsrc w_rsrc = buffer_rsrc(wbase);
   // W rows are staged in the order that the epilogues' layout needs: LDS
-  // row 128 h + 16 j + m (h: column half, j: fragment, m = 4 q + r: the
-  // fragment's row) holds tile column 128 h + 32 (j / 2) + 8 q + 4 (j % 2) + r.
-  // For the 8 LDS rows 8 jj + t of W wave-load jj that is a wave-uniform
-  // column w_col(jj) plus 8 (t / 4) + t % 4.
+  // row 128 h + 16 j + m (h: the wave's column half, j: fragment, m = 4 q + r:
+  // the fragment's row) holds tile column 128 h + 32 (j / 2) + 8 q + 4 (j % 2)
+  // + r.  SwiGLU instead pairs gate and up inside the wave: fragment j < 4
+  // holds gate column 64 h + 32 (j / 2) + 8 q + 4 (j % 2) + r of the output
+  // tile and fragment j + 4 the up column at the same place.  For the 8 LDS
+  // rows 8 jj + t of W wave-load jj either is a wave-uniform row plus
+  // 8 (t / 4) + t % 4.
   uint32_t w_voff[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
@@ -979,8 +953,14 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
     } else {                                                                                 \
       const int jj = wave * CP + (i) - CP;                                                   \
       const int jf_ = (jj >> 1) & 7;                                                         \
-      const int wc_ = 128 * (jj >> 4) + 32 * (jf_ >> 1) + 16 * (jj & 1) + 4 * (jf_ & 1);      \
-      const int64_t wr0 = w_row_base + wc_ + (wc_ >= 128 ? w_up_shift : 0);                  \
+      int64_t wr0;                                                                           \
+      if constexpr (kPair) {                                                                 \
+        const int oc_ = 64 * (jj >> 4) + 32 * ((jf_ >> 1) & 1) + 16 * (jj & 1) + 4 * (jf_ & 1); \
+        wr0 = w_row_base + oc_ + (jf_ >= 4 ? N / 2 : 0);                                     \
+      } else {                                                                               \
+        const int wc_ = 128 * (jj >> 4) + 32 * (jf_ >> 1) + 16 * (jj & 1) + 4 * (jf_ & 1);    \
+        wr0 = w_row_base + wc_;                                                              \
+      }                                                                                      \
       dma_16_buf(w_rsrc, w_voff[(i) & 1],                                                    \
                  __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(wr0 * K + (cc) * BK)),  \
                  __builtin_amdgcn_readfirstlane(st_base + (st) * C::STAGE_BYTES + L2BM * BK + jj * 1024)); \
@@ -1030,9 +1010,9 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   // its operands in registers instead of with every wave reading LDS at once.
   i32x8 fa[4], bf[2];
   f32x4 part[4];
-  float scl[4];   // per row slice: the lane's row scale times the weight block's
+  float scl[2][4];   // per row slice: the lane's row scale times the weight block's (SwiGLU: [gate, up])
   float s4n[4];
-  float swn;
+  float swn[2];
   const uint8_t* st0 = &s_stage[0][0];
 #define DSMOE_RD_A(i_, stp)                                                                    \
   do {                                                                                         \
@@ -1054,7 +1034,8 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   } while (0)
 #define DSMOE_SCL(i_)                                                  \
   do {                                                                 \
-    scl[i_] = s4n[i_] * swn;                                           \
+    scl[0][i_] = s4n[i_] * swn[0];                                     \
+    if constexpr (kPair) scl[1][i_] = s4n[i_] * swn[1];                \
   } while (0)
   // one step: MFMA k, then the promotion of MFMA k-2 (ring slot (k-2) & 3)
 #define DSMOE_STEP(k, stp)                                                                     \
@@ -1064,7 +1045,7 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
     part[(k) & 3] = mfma_chunk(bf[j_ & 1], fa[i_]);                                            \
     const int kp_ = ((k) + 30) & 31, jp_ = kp_ >> 2, ip_ = kp_ & 3;                            \
     _Pragma("unroll") for (int rr = 0; rr < 4; ++rr)                                           \
-      acc[ip_][jp_][rr] = __builtin_fmaf(part[kp_ & 3][rr], scl[ip_], acc[ip_][jp_][rr]);     \
+      acc[ip_][jp_][rr] = __builtin_fmaf(part[kp_ & 3][rr], scl[kPair && jp_ >= 4][ip_], acc[ip_][jp_][rr]); \
   } while (0)
   // per step: the MFMA, then its LDS reads, then its VALU work (a step
   // has at most 6 reads and 8 VALU instructions)
@@ -1077,7 +1058,7 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   // chunk 0's operands; the promotions of steps 0 and 1 (the previous
   // chunk's last MFMAs, of which there are none) add 0 * 0
   part[2] = part[3] = f32x4{0.f, 0.f, 0.f, 0.f};
-  scl[2] = scl[3] = 0.f;
+  scl[0][2] = scl[0][3] = scl[1][2] = scl[1][3] = 0.f;
   if (nsl > 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1085,7 +1066,8 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
       DSMOE_RD_S(i, 0);
     }
     DSMOE_RD_B(0, st0);
-    swn = s_sw[wn][0];
+    swn[0] = s_sw[kPair ? 0 : wn][0];
+    swn[1] = s_sw[1][0];
     DSMOE_SCL(0);
     DSMOE_SCL(1);
   }
@@ -1123,7 +1105,7 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
       if ((c + 2) % C::SA_BLOCK == 0) DSMOE_ISSUE_SA((c + 2) / C::SA_BLOCK);
     }
     if (nsl > 0) {
-      const float* swp = &s_sw[wn][c + 1 < kchunks ? c + 1 : c];
+      const int64_t cw = c + 1 < kchunks ? c + 1 : c;
 #pragma unroll
       for (int k = 27; k < 32; ++k) {
         DSMOE_STEP(k, stc);
@@ -1133,7 +1115,8 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
           DSMOE_RD_S(k - 28, c + 1);
           if (k == 28) {
             DSMOE_RD_B(0, stn);
-            swn = *swp;
+            swn[0] = s_sw[kPair ? 0 : wn][cw];
+            swn[1] = s_sw[1][cw];
           }
         }
         if (k == 30) DSMOE_SCL(0);  // after the promotion of MFMA 28
@@ -1146,8 +1129,8 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
   if (nsl > 0) {   // the last chunk's MFMAs 30 and 31
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      acc[2][7][rr] = __builtin_fmaf(part[2][rr], scl[2], acc[2][7][rr]);
-      acc[3][7][rr] = __builtin_fmaf(part[3][rr], scl[3], acc[3][7][rr]);
+      acc[2][7][rr] = __builtin_fmaf(part[2][rr], scl[kPair][2], acc[2][7][rr]);
+      acc[3][7][rr] = __builtin_fmaf(part[3][rr], scl[kPair][3], acc[3][7][rr]);
     }
   }
 #undef DSMOE_RD_A
@@ -1161,12 +1144,10 @@ __global__ __launch_bounds__(512) void gemm_lds2_kernel(GemmProblem p, int64_t n
 #undef DSMOE_ISSUE_SA
   if constexpr (EPI != Epilogue::kSwiGLUQuant) {
     epi_rows_lds2<EPI>(p, acc, row0, row1, wm * 64, nt * BN + wn * 128);
-  } else {  // wn = 0 waves hold the 128 gate columns, wn = 1 the matching up columns
-    __syncthreads();  // all waves are done with the stages (the exchange reuses them)
-    static_assert(4 * 2 * 16 * 64 * sizeof(f32x4) <= sizeof(s_stage) && 2 * L2BM <= L2BM * C::SA_BLOCK,
-                  "the exchange fits the stages and the row maxima the scale blocks");
-    epi_swiglu_lds2(p, acc, row0, row1, wm * 64, wn == 0, wm, nt, reinterpret_cast<f32x4*>(&s_stage[0][0]),
-                    &s_sa[0][0]);
+  } else {
+    __syncthreads();  // all waves are done with the scale blocks (the row maxima reuse them)
+    static_assert(2 * L2BM <= L2BM * C::SA_BLOCK, "the row maxima fit the scale blocks");
+    epi_swiglu_pairs(p, acc, row0, row1, wm * 64, wn, nt, &s_sa[0][0]);
   }
 }
 
