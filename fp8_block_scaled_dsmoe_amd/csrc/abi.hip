@@ -862,6 +862,7 @@ dsmoe_status dsmoe_fp8_wgrad_grouped(const uint8_t* at, const float* sa, const u
   if (!valid_dtype(ct)) return DSMOE_ERR_DTYPE;
   if (G < 1 || M <= 0 || N <= 0 || M % 128 || N % 128 || P < 0 || P % 128) return DSMOE_ERR_SHAPE;
   if (static_cast<int64_t>(G) * (M / 128) * (N / 128) > kI32Max) return DSMOE_ERR_SHAPE;
+  if (P >= (int64_t{1} << 32) / 128) return DSMOE_ERR_SHAPE;   // the kernel's 32-bit lane offsets
   if (!at || !sa || !bt || !sb || !chunk_off || !c) return DSMOE_ERR_NULL;
   if (!aligned(at, 16) || !aligned(bt, 16) || !aligned(c, 16) || !aligned(sa, 16) || !aligned(sb, 16) ||
       !aligned(chunk_off, 4))

@@ -191,113 +191,61 @@ __device__ __forceinline__ f32x4 mfma_chunk(const i32x8& a, const i32x8& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// A block owns one 128-row tile of group g's output and kWgTiles of its
+// 128-column tiles, and runs the (column tile, token tile) pairs as one
+// sequence: each step stages the pair's A and B chunks in LDS, issues the
+// loads of the next pair, and runs its MFMAs; the last token tile of a column
+// tile ends with that tile's stores.  The next pair's loads are thus in
+// flight during a tile's MFMAs and stores.  Eight waves of 32 x 64 stay within
+// 128 registers, so two blocks (16 waves) share a CU.  (One 4-wave block per
+// output tile left every tile's load latency in front of its stores and ran at
+// a third of the HBM peak; the stores alone, in the same pattern, reach the
+// rate of a plain fill.)
+//
+// The MFMAs take the B fragment as their first operand, so a lane's four
+// results of a 16 x 16 tile are four columns of one row, and B's rows are
+// staged in the order that makes a lane's 16 values over its wave's four
+// column fragments contiguous: LDS row 64 h + 16 j + 4 q + r holds tile
+// column 64 h + 16 q + 4 j + r (the two 2-bit fields swapped).  Lane group q
+// of the wave then holds columns 16 q .. 16 q + 15 of its rows and stores
+// them straight from registers.
+constexpr int kWgTiles = 4;
+constexpr int kWgThreads = 512;
+
+__device__ __forceinline__ int wg_col_swap(int r) {
+  return (r & ~0x3C) | (((r >> 2) & 3) << 4) | (((r >> 4) & 3) << 2);
+}
+
 template <bool kF32Out>
-__global__ __launch_bounds__(256) void wgrad_kernel(const uint8_t* __restrict__ at, const float* __restrict__ sat,
-                                                    const uint8_t* __restrict__ bt, const float* __restrict__ sbt,
-                                                    const int32_t* __restrict__ cho, int64_t M, int64_t N,
-                                                    int64_t P, void* __restrict__ c) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_a[2][TT * TT];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_b[2][TT * TT];
+__global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void wgrad_kernel(const uint8_t* __restrict__ at, const float* __restrict__ sat,
+                  const uint8_t* __restrict__ bt, const float* __restrict__ sbt,
+                  const int32_t* __restrict__ cho, int64_t M, int64_t N, int64_t P, void* __restrict__ c) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ab[2][2 * TT * TT];   // per stage: A [TT][TT], B [TT][TT]
   __shared__ float s_sa[2][TT], s_sb[2][TT];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1;   // rows 32 wm .., columns 64 wn ..
   const int64_t mt = M / TT, nt = N / TT;
+  const int64_t nblk = (nt + kWgTiles - 1) / kWgTiles;
   const int64_t bid = blockIdx.x;
-  const int64_t g = bid / (mt * nt);
-  const int64_t rem = bid - g * mt * nt;
-  const int64_t m0 = (rem / nt) * TT, n0 = (rem % nt) * TT;
+  const int64_t g = bid / (mt * nblk);
+  const int64_t rem = bid - g * mt * nblk;
+  const int64_t m0 = (rem / nblk) * TT;
+  const int64_t ntile0 = (rem % nblk) * kWgTiles;
+  const int64_t ntile1 = min<int64_t>(ntile0 + kWgTiles, nt);
   // (tiles past the P columns are never read, whatever chunk_off says)
   const int32_t t0 = cho[g], t1 = min(cho[g + 1], static_cast<int32_t>(P / TT));
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // this thread's share of a chunk: 4 segments of A and of B (row idx >> 3,
-  // segment idx & 7 of the row's 128 bytes) and one scale
-  u32x4 ra[4], rb[4];
-  float rs = 0.f;
-#define DSMOE_WG_LOAD(tt)                                                                 \
-  do {                                                                                    \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                       \
-      const int idx = tid + 256 * q;                                                      \
-      const int64_t off = static_cast<int64_t>(tt) * TT + (idx & 7) * 16;                 \
-      ra[q] = *reinterpret_cast<const u32x4*>(at + (m0 + (idx >> 3)) * P + off);         \
-      rb[q] = *reinterpret_cast<const u32x4*>(bt + (n0 + (idx >> 3)) * P + off);         \
-    }                                                                                     \
-    rs = tid < TT ? sat[static_cast<int64_t>(tt) * M + m0 + tid]                          \
-                  : sbt[static_cast<int64_t>(tt) * N + n0 + tid - TT];                    \
-  } while (0)
+  const int32_t ntt = t1 > t0 ? t1 - t0 : 0;
 
   const int frow = lane & 15;
-  const int fseg = (lane >> 4) * 2;
-  if (t0 < t1) DSMOE_WG_LOAD(t0);
-  for (int32_t tt = t0; tt < t1; ++tt) {
-    const int buf = (tt - t0) & 1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = tid + 256 * q;
-      *reinterpret_cast<u32x4*>(&s_a[buf][swz(idx >> 3, idx & 7)]) = ra[q];
-      *reinterpret_cast<u32x4*>(&s_b[buf][swz(idx >> 3, idx & 7)]) = rb[q];
-    }
-    if (tid < TT) s_sa[buf][tid] = rs; else s_sb[buf][tid - TT] = rs;
-    __syncthreads();
-    if (tt + 1 < t1) DSMOE_WG_LOAD(tt + 1);
-    i32x8 fa[4], fb[4];
-    float sa[4][4], sb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 64 + i * 16 + frow;
-      fa[i] = cat8(*reinterpret_cast<const u32x4*>(&s_a[buf][swz(r, fseg)]),
-                   *reinterpret_cast<const u32x4*>(&s_a[buf][swz(r, fseg + 1)]));
-      const f32x4 s4 = *reinterpret_cast<const f32x4*>(&s_sa[buf][wm * 64 + i * 16 + (lane >> 4) * 4]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) sa[i][q] = s4[q];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wn * 64 + j * 16 + frow;
-      fb[j] = cat8(*reinterpret_cast<const u32x4*>(&s_b[buf][swz(r, fseg)]),
-                   *reinterpret_cast<const u32x4*>(&s_b[buf][swz(r, fseg + 1)]));
-      sb[j] = s_sb[buf][r];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 part = mfma_chunk(fa[i], fb[j]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(part[q], sa[i][q] * sb[j], acc[i][j][q]);
-      }
-  }
-#undef DSMOE_WG_LOAD
-  __syncthreads();   // every wave is done with the stages: the epilogue reuses s_a
-
-  // each 16-row slice of the wave tile through the wave's LDS scratch, then a
-  // lane writes 16 contiguous columns of one row
-  constexpr int S = 64 + 4;
-  float* scratch = reinterpret_cast<float*>(&s_a[0][0]) + wave * 16 * S;
+  const int fq = lane >> 4;
   const size_t esz = kF32Out ? 4 : 2;
   uint8_t* cg = static_cast<uint8_t*>(c) + static_cast<size_t>(g) * M * N * esz;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) scratch[((lane >> 4) * 4 + q) * S + j * 16 + frow] = acc[i][j][q];
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_wave_barrier();
-    const int lr = lane >> 2, lc = (lane & 3) * 16;
-    float v[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = scratch[lr * S + lc + e];
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_wave_barrier();
-    const int64_t row = m0 + wm * 64 + i * 16 + lr;
-    const int64_t col = n0 + wn * 64 + lc;
+  // a lane's 16 contiguous columns 64 wn + 16 fq .. of row slice i of column tile n
+  auto store16 = [&](int i, int64_t n, const float (&v)[16]) {
+    const int64_t row = m0 + wm * 32 + i * 16 + frow;
+    const int64_t col = n * TT + wn * 64 + fq * 16;
     if constexpr (kF32Out) {
       f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(cg) + row * N + col);
 #pragma unroll
@@ -308,12 +256,124 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const uint8_t* __restrict__ 
       for (int q = 0; q < 2; ++q) {
         u32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = f32x2_to_bf16x2(v[8 * q + 2 * e], v[8 * q + 2 * e + 1]);
+        for (int e = 0; e < 4; ++e) w[e] = f32x2_to_bf16x2(v[8 * q + 2 * e], v[8 * q + 2 * e + 1]);
         dst[q] = w;
       }
     }
+  };
+
+  if (ntt == 0) {   // a group with no token: its weight gradient is zero
+    float z[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = 0.0f;
+    for (int64_t n = ntile0; n < ntile1; ++n)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) store16(i, n, z);
+    return;
   }
+
+  // acc[i][j]: row slice i, column fragment j; lane element r is tile column
+  // 64 wn + 16 fq + 4 j + r of row 32 wm + 16 i + frow
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // this thread's share of a pair's chunks: 2 segments of A and of B (row
+  // idx >> 3, segment idx & 7 of the row's 128 bytes) and, for the first 256
+  // threads, one scale
+  u32x4 ra[2], rb[2];
+  float rs = 0.f;
+  // per-lane byte offsets of the loads within a 128-row block of A or B
+  // (fixed over the steps: 127 rows of P bytes, far below 2^32); a step adds
+  // the wave-uniform row-tile, column-tile and token-tile offsets
+  uint32_t lane_off[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int idx = tid + kWgThreads * q;
+    lane_off[q] = static_cast<uint32_t>((idx >> 3) * P + (idx & 7) * 16);
+  }
+  const uint8_t* a_tile = at + m0 * P;
+#define DSMOE_WG_LOAD(tt, n0)                                                             \
+  do {                                                                                    \
+    const int64_t koff = static_cast<int64_t>(tt) * TT;                                   \
+    const uint8_t* abase = a_tile + koff;                                                 \
+    const uint8_t* bbase = bt + (n0) * P + koff;                                          \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                       \
+      ra[q] = *reinterpret_cast<const u32x4*>(abase + lane_off[q]);                       \
+      rb[q] = *reinterpret_cast<const u32x4*>(bbase + lane_off[q]);                       \
+    }                                                                                     \
+    if (tid < TT)                                                                         \
+      rs = sat[static_cast<int64_t>(tt) * M + m0 + tid];                                  \
+    else if (tid < 2 * TT)                                                                \
+      rs = sbt[static_cast<int64_t>(tt) * N + (n0) + (tid - TT)];                         \
+  } while (0)
+
+  const int fseg = fq * 2;
+  const int64_t steps = (ntile1 - ntile0) * ntt;
+  DSMOE_WG_LOAD(t0, ntile0 * TT);
+  int64_t n = ntile0;
+  int32_t tt = t0;
+  for (int64_t st = 0; st < steps; ++st) {
+    const int buf = static_cast<int>(st & 1);
+    uint8_t* sa_ = &s_ab[buf][0];
+    uint8_t* sb_ = &s_ab[buf][TT * TT];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + kWgThreads * q;
+      *reinterpret_cast<u32x4*>(&sa_[swz(idx >> 3, idx & 7)]) = ra[q];
+      *reinterpret_cast<u32x4*>(&sb_[swz(wg_col_swap(idx >> 3), idx & 7)]) = rb[q];
+    }
+    if (tid < TT) s_sa[buf][tid] = rs;             // by tile row
+    else if (tid < 2 * TT) s_sb[buf][tid - TT] = rs;   // by tile column
+    __syncthreads();
+    // the next pair: the next token tile, or the next column tile's first
+    const bool tile_end = tt + 1 == t1;
+    const int32_t tt_n = tile_end ? t0 : tt + 1;
+    const int64_t n_n = tile_end ? n + 1 : n;
+    if (st + 1 < steps) DSMOE_WG_LOAD(tt_n, n_n * TT);
+    i32x8 fa[2];
+    float sa[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = wm * 32 + i * 16 + frow;
+      fa[i] = cat8(*reinterpret_cast<const u32x4*>(&sa_[swz(r, fseg)]),
+                   *reinterpret_cast<const u32x4*>(&sa_[swz(r, fseg + 1)]));
+      sa[i] = s_sa[buf][r];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn * 64 + j * 16 + frow;   // LDS row (staged order)
+      const i32x8 fb = cat8(*reinterpret_cast<const u32x4*>(&sb_[swz(r, fseg)]),
+                            *reinterpret_cast<const u32x4*>(&sb_[swz(r, fseg + 1)]));
+      const f32x4 sb = *reinterpret_cast<const f32x4*>(&s_sb[buf][wn * 64 + fq * 16 + j * 4]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const f32x4 part = mfma_chunk(fb, fa[i]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(part[q], sa[i] * sb[q], acc[i][j][q]);
+      }
+    }
+    if (tile_end) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[4 * j + q] = acc[i][j][q];
+        store16(i, n, v);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    tt = tt_n;
+    n = n_n;
+  }
+#undef DSMOE_WG_LOAD
 }
 
 // ---------------------------------------------------------------------------
@@ -448,12 +508,12 @@ hipError_t launch_quant_tokens(const void* src, bool f32, int64_t C, const int32
 
 hipError_t launch_wgrad(const uint8_t* at, const float* sat, const uint8_t* bt, const float* sbt, const int32_t* cho,
                         int32_t G, int64_t M, int64_t N, int64_t P, void* c, bool f32, hipStream_t s) {
-  const int64_t blocks = static_cast<int64_t>(G) * (M / TT) * (N / TT);
+  const int64_t blocks = static_cast<int64_t>(G) * (M / TT) * ((N / TT + kWgTiles - 1) / kWgTiles);
   if (blocks == 0) return hipSuccess;
   if (f32)
-    wgrad_kernel<true><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(at, sat, bt, sbt, cho, M, N, P, c);
+    wgrad_kernel<true><<<dim3(static_cast<unsigned>(blocks)), kWgThreads, 0, s>>>(at, sat, bt, sbt, cho, M, N, P, c);
   else
-    wgrad_kernel<false><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(at, sat, bt, sbt, cho, M, N, P, c);
+    wgrad_kernel<false><<<dim3(static_cast<unsigned>(blocks)), kWgThreads, 0, s>>>(at, sat, bt, sbt, cho, M, N, P, c);
   return hipGetLastError();
 }
 

@@ -498,7 +498,8 @@ dsmoe_status dsmoe_quant_tokens_128(const void* src, int src_type, int64_t n_src
  * For the down projection o = a W2^T: at = quantised do^T (M = H), bt =
  * quantised a^T (N = I), c = dW2 [G][H][I].  For the gate/up projection:
  * at = quantised dh^T (M = 2I), bt = quantised x^T (N = H), c = dW13.
- * Requires M, N positive multiples of 128, 1 <= G, P a multiple of 128.
+ * Requires M, N positive multiples of 128, 1 <= G, P a multiple of 128 and
+ * 128 * P < 2^32 (DSMOE_ERR_SHAPE otherwise).
  */
 dsmoe_status dsmoe_fp8_wgrad_grouped(const uint8_t* at, const float* sa, const uint8_t* bt, const float* sb,
                                      const int32_t* chunk_off, int32_t G, int64_t M, int64_t N, int64_t P,

@@ -187,6 +187,21 @@ def test_gemm_validation_errors():
     assert L.dsmoe_fp8_grouped_gemm(a, a, None, a, 1, 64, a, a, 128, 32768 + 128, a, 0, None) == 2
 
 
+def test_wgrad_validation_errors():
+    import fp8_block_scaled_dsmoe_amd as d
+    L = d.lib
+    a = _vp(ALIGNED)
+    # M, N multiples of 128, P a multiple of 128, a known output dtype
+    assert L.dsmoe_fp8_wgrad_grouped(a, a, a, a, a, 1, 100, 128, 128, a, 0, None) == 2
+    assert L.dsmoe_fp8_wgrad_grouped(a, a, a, a, a, 1, 128, 128, 100, a, 0, None) == 2
+    assert L.dsmoe_fp8_wgrad_grouped(a, a, a, a, a, 0, 128, 128, 128, a, 0, None) == 2
+    assert L.dsmoe_fp8_wgrad_grouped(a, a, a, a, a, 1, 128, 128, 128, a, 5, None) == 4
+    # the kernel's per-lane offsets cover 128 rows of P bytes in 32 bits
+    big = (1 << 32) // 128 // 128 * 128
+    assert L.dsmoe_fp8_wgrad_grouped(a, a, a, a, a, 1, 128, 128, big, a, 0, None) == 2
+    assert L.dsmoe_fp8_wgrad_grouped(a, a, a, a, None, 1, 128, 128, big - 128, a, 0, None) == 1
+
+
 def test_moe_forward_validation_errors():
     import fp8_block_scaled_dsmoe_amd as d
     L = d.lib

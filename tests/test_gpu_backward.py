@@ -151,6 +151,13 @@ def test_wgrad_grouped_ragged_groups(out_dtype):
     _wgrad_case(256, 384, [0, 1, 129, 0, 300, 64], out_dtype, 21, "ragged")
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_wgrad_grouped_column_tile_runs(out_dtype):
+    """11 column tiles, which a block takes 8 at a time (a full run and a run
+    of 3), over empty groups, one row, two token tiles and a whole tile."""
+    _wgrad_case(256, 1408, [0, 130, 1, 0, 257, 128], out_dtype, 23, "column-tile runs")
+
+
 @pytest.mark.parametrize("M,N,what", [(7168, 2048, "dW2 of a V3 expert"), (4096, 7168, "dW13 of a V3 expert")])
 def test_wgrad_v3_shapes(M, N, what):
     """One V3 expert with 300 rows (three token tiles): dW2 [7168][2048] and
