@@ -144,6 +144,28 @@ def measured_mfma(workload):
     return None if t is None or "mfma_busy_frac" not in t else t["mfma_busy_frac"]
 
 
+WGRAD_SOURCES = ["backward.hip", "common.h", "kernels.h"]
+
+
+def wgrad_w13_traffic(wgrad_dtype):
+    """HBM bytes of the W13 weight-gradient launch from its committed counter
+    record (bf16 gradients), or None when the record was taken on other
+    sources of that kernel."""
+    import hashlib
+    if wgrad_dtype != "bf16":
+        return None
+    try:
+        with open(os.path.join(ROOT, "profiles", "counters_wgrad_w13_v3_prefill_backward.json")) as fh:
+            t = json.load(fh)
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for f in WGRAD_SOURCES:
+        with open(os.path.join(ROOT, "fp8_block_scaled_dsmoe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return int(t["traffic_bytes_per_launch"]) if t.get("sources_sha256") == h.hexdigest() else None
+
+
 def host_info():
     """CPU model and the BLAS NumPy uses (name, version, threads)."""
     model = None
@@ -749,7 +771,8 @@ def run_backward(args, torch):
                                f"T={T}, H={H}, E={E}, top-{K}, I={I}",
                    "T": T, "H": H, "E": E, "K": K, "I": I},
         "roofline": {"bound": "hbm", "achieved": round(gb(wg13_bytes, wg13_ms), 2), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(gb(wg13_bytes, wg13_ms) / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gb(wg13_bytes, wg13_ms) / PEAK_HBM_GBPS, 4),
+                     "traffic": wgrad_w13_traffic(args.wgrad_dtype),
                      "kernel": "weight gradient of W13 (grouped FP8 Wgrad GEMM over each expert's tokens)",
                      "algorithmic_bytes": int(wg13_bytes), "avg_ms": round(wg13_ms, 4)},
         "grouped_gemm_tflops": round(tf(gemm_flops, ms), 2),
