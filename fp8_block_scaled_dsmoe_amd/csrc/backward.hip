@@ -171,13 +171,12 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const void* __restric
 }
 
 // ---------------------------------------------------------------------------
-// wgrad_kernel: one 128 x 128 tile of c_g per block, four waves of 64 x 64
-// (4 x 4 MFMA tiles).  The K loop runs over the group's token tiles: A and B
+// wgrad_kernel: c_g = A_g B_g^T over the group's token tiles.  A and B
 // chunks (128 rows x 128 bytes each) and their per-row scales are loaded to
-// registers one tile ahead, stored to a double-buffered LDS stage, and
-// multiplied there; each MFMA (zero accumulator) gives one tile's partial
-// sum, promoted as acc += P * (sa[m] * sb[n]).  A group without tokens gets
-// zeros.
+// registers one (column tile, token tile) pair ahead, stored to a
+// double-buffered LDS stage, and multiplied there; each MFMA (zero
+// accumulator) gives one token tile's partial sum, promoted as
+// acc += P * (sa[m] * sb[n]).  A group without tokens gets zeros.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz(int row, int seg) { return row * TT + ((seg ^ swz_key(row)) << 4); }
