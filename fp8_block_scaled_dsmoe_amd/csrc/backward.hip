@@ -29,6 +29,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TT = 128;   // rows per token tile = the promotion interval
+constexpr int kXcds = 8;  // XCDs, over which a launch's blocks are dispatched round-robin
 
 // ---------------------------------------------------------------------------
 // Token tiles of each group: cho[g] = sum over g' < g of ceil(n_g' / 128)
@@ -219,7 +220,8 @@ template <bool kF32Out>
 __global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void wgrad_kernel(const uint8_t* __restrict__ at, const float* __restrict__ sat,
                   const uint8_t* __restrict__ bt, const float* __restrict__ sbt,
-                  const int32_t* __restrict__ cho, int64_t M, int64_t N, int64_t P, void* __restrict__ c) {
+                  const int32_t* __restrict__ cho, int64_t M, int64_t N, int64_t P, void* __restrict__ c,
+                  int32_t pm, int32_t pn) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_ab[2][2 * TT * TT];   // per stage: A [TT][TT], B [TT][TT]
   __shared__ float s_sa[2][TT], s_sb[2][TT];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -227,11 +229,33 @@ void wgrad_kernel(const uint8_t* __restrict__ at, const float* __restrict__ sat,
   const int wm = wave >> 1, wn = wave & 1;   // rows 32 wm .., columns 64 wn ..
   const int64_t mt = M / TT, nt = N / TT;
   const int64_t nblk = (nt + kWgTiles - 1) / kWgTiles;
-  const int64_t bid = blockIdx.x;
-  const int64_t g = bid / (mt * nblk);
-  const int64_t rem = bid - g * mt * nblk;
-  const int64_t m0 = (rem / nblk) * TT;
-  const int64_t ntile0 = (rem % nblk) * kWgTiles;
+  // (block indices and counts below 2^31: the grid is at most that)
+  const int32_t bid = static_cast<int32_t>(blockIdx.x);
+  const int32_t mt32 = static_cast<int32_t>(mt), nb32 = static_cast<int32_t>(nblk);
+  int32_t g, mtile, nrun;
+  if (pm > 0) {
+    // Blocks are dispatched round-robin over the kXcds XCDs.  Every round of
+    // kXcds blocks belongs to one group (the same work on every XCD), and XCD
+    // x takes the part (x / pn, x % pn) of the group's pm x pn parts of
+    // (row tile, column run) pairs: a row tile's A chunks are then read by pn
+    // XCDs and a column run's B chunks by pm, instead of by every XCD.
+    const int32_t mq = mt32 / pm, nq = nb32 / pn, per_x = mq * nq;
+    const int32_t slot = bid / kXcds, x = bid % kXcds;
+    g = slot / per_x;
+    const int32_t j = slot - g * per_x;
+    mtile = (x / pn) * mq + j / nq;
+    nrun = (x % pn) * nq + j % nq;
+  } else {
+    g = bid / (mt32 * nb32);
+    const int32_t rem = bid - g * mt32 * nb32;
+    mtile = rem / nb32;
+    nrun = rem % nb32;
+  }
+  g = __builtin_amdgcn_readfirstlane(g);
+  mtile = __builtin_amdgcn_readfirstlane(mtile);
+  nrun = __builtin_amdgcn_readfirstlane(nrun);
+  const int64_t m0 = static_cast<int64_t>(mtile) * TT;
+  const int64_t ntile0 = static_cast<int64_t>(nrun) * kWgTiles;
   const int64_t ntile1 = min<int64_t>(ntile0 + kWgTiles, nt);
   // (tiles past the P columns are never read, whatever chunk_off says)
   const int32_t t0 = cho[g], t1 = min(cho[g + 1], static_cast<int32_t>(P / TT));
@@ -507,12 +531,28 @@ hipError_t launch_quant_tokens(const void* src, bool f32, int64_t C, const int32
 
 hipError_t launch_wgrad(const uint8_t* at, const float* sat, const uint8_t* bt, const float* sbt, const int32_t* cho,
                         int32_t G, int64_t M, int64_t N, int64_t P, void* c, bool f32, hipStream_t s) {
-  const int64_t blocks = static_cast<int64_t>(G) * (M / TT) * ((N / TT + kWgTiles - 1) / kWgTiles);
+  const int64_t mt = M / TT, nblk = (N / TT + kWgTiles - 1) / kWgTiles;
+  const int64_t blocks = static_cast<int64_t>(G) * mt * nblk;
   if (blocks == 0) return hipSuccess;
+  // split of a group's (row tile, column run) pairs over the XCDs: pm row
+  // parts x pn column parts, pm * pn = kXcds, the one that reads the fewest
+  // operand bytes (pn copies of A's M rows, pm of B's N); 0 = none fits
+  int32_t pm = 0, pn = 0;
+  int64_t best = 0;
+  for (int32_t q = 1; q <= kXcds; q *= 2) {
+    const int32_t r = kXcds / q;   // q column parts, r row parts
+    if (mt % r != 0 || nblk % q != 0) continue;
+    const int64_t bytes = q * M + r * N;
+    if (pm == 0 || bytes < best) {
+      pm = r;
+      pn = q;
+      best = bytes;
+    }
+  }
   if (f32)
-    wgrad_kernel<true><<<dim3(static_cast<unsigned>(blocks)), kWgThreads, 0, s>>>(at, sat, bt, sbt, cho, M, N, P, c);
+    wgrad_kernel<true><<<dim3(static_cast<unsigned>(blocks)), kWgThreads, 0, s>>>(at, sat, bt, sbt, cho, M, N, P, c, pm, pn);
   else
-    wgrad_kernel<false><<<dim3(static_cast<unsigned>(blocks)), kWgThreads, 0, s>>>(at, sat, bt, sbt, cho, M, N, P, c);
+    wgrad_kernel<false><<<dim3(static_cast<unsigned>(blocks)), kWgThreads, 0, s>>>(at, sat, bt, sbt, cho, M, N, P, c, pm, pn);
   return hipGetLastError();
 }
 

@@ -158,6 +158,13 @@ def test_wgrad_grouped_column_tile_runs(out_dtype):
     _wgrad_case(256, 1408, [0, 130, 1, 0, 257, 128], out_dtype, 23, "column-tile runs")
 
 
+@pytest.mark.parametrize("M,N,split", [(1024, 512, "8 x 1"), (1024, 2048, "2 x 4"), (2048, 1024, "4 x 2")])
+def test_wgrad_grouped_xcd_splits(M, N, split):
+    """Shapes whose (row tile, column run) pairs the launch splits over the
+    XCDs as 8 x 1, 2 x 4 and 4 x 2 parts, over ragged and empty groups."""
+    _wgrad_case(M, N, [130, 0, 1, 257, 64], torch.float32, M + 3 * N, f"xcd split {split}")
+
+
 @pytest.mark.parametrize("M,N,what", [(7168, 2048, "dW2 of a V3 expert"), (4096, 7168, "dW13 of a V3 expert")])
 def test_wgrad_v3_shapes(M, N, what):
     """One V3 expert with 300 rows (three token tiles): dW2 [7168][2048] and
